@@ -1,0 +1,126 @@
+/*
+ * mhc.h -- C ABI of the MI355X (gfx950) mHC site library (libmhc.so).
+ *
+ * The library runs the per-token, per-site mHC (manifold-constrained
+ * hyper-connections) residual program on one GPU, as two calls:
+ *
+ *   mhc_site_pre   mixes GEMV + RMS rescale + gates + Sinkhorn + collapse
+ *   mhc_site_post  post mix of the branch output back into the streams
+ *
+ * The operation is the one described on the docs.rs page "memra_engine
+ * 0.125.0 src/memra_engine/hyper.rs", module documentation ("ARITHMETIC
+ * CONTRACT" and "MEMORY LAYOUT"), with the row order of the mixes given by the
+ * doc comment of HyperTopology::rows and the post mix by the doc comment of the
+ * page's `post` function.  The gate forms the page leaves open are fixed here:
+ * pre = sigmoid, post = 2*sigmoid, comb = Sinkhorn-Knopp of exp(.), one
+ * iteration being a row pass then a column pass, each dividing by (sum + eps).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers to dense fp32 arrays owned by the
+ *    caller; each must be 16-byte aligned.  Outputs are fully overwritten (no
+ *    zeroing needed, prior contents never read).  The library keeps no pointer
+ *    after a call returns.
+ *  - Layout is token-major: x[T][S][H], element (t,k,i) at (t*S+k)*H+i, so one
+ *    token's S*H slab is contiguous.  S = streams, H = hidden, R = (2+S)*S.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *    work; they never synchronise the host.  Results are ready once the stream
+ *    reaches the enqueued work.
+ *  - Every argument check happens on the host BEFORE any GPU work is enqueued;
+ *    a call that returns an error has enqueued nothing.
+ *  - Calls on the same device share one library-owned scratch area (partial
+ *    sums of the split reduction).  Two calls enqueued on DIFFERENT streams of
+ *    the same device must not run concurrently; calls on one stream are always
+ *    safe.  The scratch is allocated by the first call that needs it on each
+ *    device (a one-time hipMalloc) and lives until the process ends.
+ *  - Supported shapes: 1 <= S <= 8, H >= 4 with H % 4 == 0, T >= 0
+ *    (T == 0 is a no-op), iters >= 1, eps > 0 and finite, T*S*H < 2^31.
+ *  - Numeric domain: finite inputs with |scale*m + base| below about 80, so
+ *    that exp() stays finite in fp32; outside it results are unspecified.
+ */
+#ifndef MHC_H
+#define MHC_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+enum {
+  MHC_OK = 0,
+  MHC_EINVAL = 1,      /* bad size, count, eps, iteration count or NULL pointer */
+  MHC_EALIGN = 2,      /* H % 4 != 0 or a pointer not 16-byte aligned            */
+  MHC_EUNSUPPORTED = 3,/* valid arguments this build does not handle (S > 8)    */
+  MHC_EHIP = 4,        /* the HIP runtime reported an error (launch, allocation) */
+  MHC_EOVERLAP = 5     /* an output buffer overlaps an input buffer              */
+};
+
+/*
+ * mhc_site_pre -- the pre half of one site, for T tokens.
+ *
+ * Per token t (hyper.rs module doc, arithmetic contract, first four lines):
+ *   ss      = sum_i x[t,i]^2 over the whole S*H slab;  rinv = 1/sqrt(ss/(S*H) + eps)
+ *   m[r]    = rinv * sum_i fn_w[r,i] * x[t,i]                         r < R
+ *   z[r]    = scale[g] * m[r] + base[r]   g = 0 for rows [0,S), 1 for [S,2S),
+ *                                         2 for the S*S comb rows [2S,R)
+ *   pre[t,c]   = 1/(1+exp(-z[c]))
+ *   post[t,k]  = 2/(1+exp(-z[S+k]))
+ *   comb[t,j,k]= Sinkhorn of exp(z[2S + j*S + k]) over `iters` rounds
+ *                (j = source stream, k = target stream)
+ *   y[t,i]     = sum_c pre[t,c] * x[t,c,i]
+ *
+ * Arguments:
+ *   x      [T][S][H]  stream state (read only)
+ *   fn_w   [R][S*H]   mixes weight, row-major (read only)
+ *   scale  [3]        pre, post and comb scales (read only)
+ *   base   [R]        per-row bias (read only)
+ *   T, streams (=S), hidden (=H), iters, eps   as above
+ *   pre    [T][S]     out
+ *   post   [T][S]     out
+ *   comb   [T][S][S]  out
+ *   y      [T][H]     out (the branch input)
+ *   stream            hipStream_t or NULL
+ * Outputs must not overlap x, fn_w, scale, base or each other (MHC_EOVERLAP).
+ * Returns MHC_OK or an error code above.
+ */
+int mhc_site_pre(const float* x, const float* fn_w, const float* scale, const float* base,
+                 int T, int streams, int hidden, int iters, float eps,
+                 float* pre, float* post, float* comb, float* y, void* stream);
+
+/*
+ * mhc_site_post -- the post half of one site (hyper.rs, doc comment of `post`):
+ *   x_out[t,k,i] = post[t,k] * f[t,i] + sum_j comb[t,j,k] * x[t,j,i]
+ * where x is the SITE's input state (the same x given to mhc_site_pre) and f the
+ * branch output for the site.
+ *
+ * Arguments:
+ *   x      [T][S][H]  site input state (read only)
+ *   f      [T][H]     branch output (read only)
+ *   post   [T][S]     post gates (read only)
+ *   comb   [T][S][S]  combination matrices, comb[t][j][k] (read only)
+ *   T, streams (=S), hidden (=H)
+ *   x_out  [T][S][H]  out; must not overlap any input (MHC_EOVERLAP)
+ *   stream            hipStream_t or NULL
+ * Returns MHC_OK or an error code above.
+ */
+int mhc_site_post(const float* x, const float* f, const float* post, const float* comb,
+                  int T, int streams, int hidden, float* x_out, void* stream);
+
+/*
+ * Argument checks alone: return exactly the code mhc_site_pre / mhc_site_post
+ * would return for these arguments before enqueuing any work (MHC_OK if the
+ * call would go ahead).  They make no HIP call and are safe without a GPU.
+ */
+int mhc_site_pre_check(const float* x, const float* fn_w, const float* scale, const float* base,
+                       int T, int streams, int hidden, int iters, float eps,
+                       const float* pre, const float* post, const float* comb, const float* y);
+int mhc_site_post_check(const float* x, const float* f, const float* post, const float* comb,
+                        int T, int streams, int hidden, const float* x_out);
+
+/* Static text for a return code (never NULL). */
+const char* mhc_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MHC_H */

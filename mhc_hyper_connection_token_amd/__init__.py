@@ -1,0 +1,145 @@
+"""MI355X (gfx950) mHC site library: Python binding of libmhc.so.
+
+The two calls mirror the C ABI in ``include/mhc.h``:
+
+* :func:`site_pre`  -> ``mhc_site_pre``  (mixes GEMV, RMS rescale, gates, Sinkhorn, collapse)
+* :func:`site_post` -> ``mhc_site_post`` (post mix)
+
+This module only marshals arguments: it checks that the operands are contiguous
+float32 CUDA (HIP) tensors of matching shapes, allocates outputs with
+``torch.empty`` when none are given, and passes raw device pointers and the
+current HIP stream to the library.  Every step of the computation runs in the
+library's kernels.  There is no fallback: if ``libmhc.so`` is missing the calls
+raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["site_pre", "site_post", "site_pre_check", "site_post_check", "load_library",
+           "MhcError", "LIB_PATH", "EXPORTED_SYMBOLS", "STATUS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmhc.so")
+
+EXPORTED_SYMBOLS = ("mhc_site_pre", "mhc_site_post", "mhc_site_pre_check",
+                    "mhc_site_post_check", "mhc_status_string")
+
+STATUS = {0: "MHC_OK", 1: "MHC_EINVAL", 2: "MHC_EALIGN", 3: "MHC_EUNSUPPORTED",
+          4: "MHC_EHIP", 5: "MHC_EOVERLAP"}
+
+_lib = None
+
+
+class MhcError(RuntimeError):
+    def __init__(self, call: str, status: int, text: str):
+        super().__init__(f"{call} failed: {STATUS.get(status, status)} ({text})")
+        self.status = status
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libmhc.so from this package directory (built by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first "
+                           "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, fl, i = ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+    lib.mhc_site_pre.argtypes = [vp, vp, vp, vp, i, i, i, i, fl, vp, vp, vp, vp, vp]
+    lib.mhc_site_pre.restype = i
+    lib.mhc_site_post.argtypes = [vp, vp, vp, vp, i, i, i, vp, vp]
+    lib.mhc_site_post.restype = i
+    lib.mhc_site_pre_check.argtypes = [vp, vp, vp, vp, i, i, i, i, fl, vp, vp, vp, vp]
+    lib.mhc_site_pre_check.restype = i
+    lib.mhc_site_post_check.argtypes = [vp, vp, vp, vp, i, i, i, vp]
+    lib.mhc_site_post_check.restype = i
+    lib.mhc_status_string.argtypes = [i]
+    lib.mhc_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _status_text(lib, rc: int) -> str:
+    return lib.mhc_status_string(rc).decode()
+
+
+def _dev(t, name, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def site_pre(x, fn_w, scale, base, iters: int, eps: float, *, out=None, stream=None):
+    """Pre half of a site.  x: [T,S,H]; fn_w: [(2+S)*S, S*H]; scale: [3]; base: [(2+S)*S].
+    Returns (pre [T,S], post [T,S], comb [T,S,S], y [T,H]); `out` may supply that tuple."""
+    import torch
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be [T, S, H]")
+    T, S, H = x.shape
+    R = (2 + S) * S
+    px = _dev(x, "x")
+    pw = _dev(fn_w, "fn_w", (R, S * H))
+    ps = _dev(scale, "scale", (3,))
+    pb = _dev(base, "base", (R,))
+    if out is None:
+        out = (torch.empty((T, S), device=x.device, dtype=torch.float32),
+               torch.empty((T, S), device=x.device, dtype=torch.float32),
+               torch.empty((T, S, S), device=x.device, dtype=torch.float32),
+               torch.empty((T, H), device=x.device, dtype=torch.float32))
+    pre, post, comb, y = out
+    ptrs = (_dev(pre, "pre", (T, S)), _dev(post, "post", (T, S)),
+            _dev(comb, "comb", (T, S, S)), _dev(y, "y", (T, H)))
+    rc = lib.mhc_site_pre(px, pw, ps, pb, T, S, H, int(iters), float(eps), *ptrs,
+                          _stream_handle(stream))
+    if rc != 0:
+        raise MhcError("mhc_site_pre", rc, _status_text(lib, rc))
+    return out
+
+
+def site_post(x, f, post, comb, *, out=None, stream=None):
+    """Post half of a site: x' [T,S,H] from x [T,S,H], f [T,H], post [T,S], comb [T,S,S]."""
+    import torch
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be [T, S, H]")
+    T, S, H = x.shape
+    px = _dev(x, "x")
+    pf = _dev(f, "f", (T, H))
+    pp = _dev(post, "post", (T, S))
+    pc = _dev(comb, "comb", (T, S, S))
+    if out is None:
+        out = torch.empty((T, S, H), device=x.device, dtype=torch.float32)
+    po = _dev(out, "out", (T, S, H))
+    rc = lib.mhc_site_post(px, pf, pp, pc, T, S, H, po, _stream_handle(stream))
+    if rc != 0:
+        raise MhcError("mhc_site_post", rc, _status_text(lib, rc))
+    return out
+
+
+def site_pre_check(x_ptr, fn_w_ptr, scale_ptr, base_ptr, T, S, H, iters, eps,
+                   pre_ptr, post_ptr, comb_ptr, y_ptr) -> int:
+    """The library's host-side argument check on raw addresses (no HIP call)."""
+    lib = load_library()
+    return lib.mhc_site_pre_check(x_ptr, fn_w_ptr, scale_ptr, base_ptr, T, S, H, iters,
+                                  float(eps), pre_ptr, post_ptr, comb_ptr, y_ptr)
+
+
+def site_post_check(x_ptr, f_ptr, post_ptr, comb_ptr, T, S, H, out_ptr) -> int:
+    lib = load_library()
+    return lib.mhc_site_post_check(x_ptr, f_ptr, post_ptr, comb_ptr, T, S, H, out_ptr)

@@ -1,0 +1,192 @@
+// mhc_api.hip -- the C ABI of libmhc (declared in include/mhc.h): argument
+// checks, the per-device scratch area, and the choice of kernels per shape.
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "mhc.h"
+#include "mhc_kernels.h"
+
+namespace {
+
+constexpr long kMaxElems = 1L << 31;  // T*S*H must stay below this (int indexing)
+constexpr int kMaxTokens = 1 << 23;   // bounds the flattened launch grids
+
+int check_ptr(const void* p) {
+  if (!p) return MHC_EINVAL;
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return MHC_EALIGN;
+  return MHC_OK;
+}
+
+struct Span {
+  uintptr_t lo, hi;
+};
+Span span(const void* p, size_t bytes) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Span{a, a + bytes};
+}
+bool overlaps(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+int check_shape(int T, int S, int H) {
+  if (T < 0 || S < 1 || H < 1) return MHC_EINVAL;
+  if (S > 8) return MHC_EUNSUPPORTED;
+  if (H % 4 != 0) return MHC_EALIGN;
+  if ((long)T * S * H >= kMaxElems || T >= kMaxTokens) return MHC_EUNSUPPORTED;
+  return MHC_OK;
+}
+
+// Library-owned scratch, one buffer per device, grown on demand.  Growth waits
+// for the device to go idle before the old buffer is released, so work already
+// enqueued that still reads the old buffer is not disturbed.
+struct DeviceScratch {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_scratch_mu;
+DeviceScratch g_scratch[64];
+
+int get_scratch(size_t bytes, float** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MHC_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  DeviceScratch& s = g_scratch[dev];
+  if (s.bytes < bytes) {
+    size_t want = bytes < (size_t(1) << 20) ? (size_t(1) << 20) : bytes + bytes / 4;
+    if (s.ptr) {
+      if (hipDeviceSynchronize() != hipSuccess) return MHC_EHIP;
+      if (hipFree(s.ptr) != hipSuccess) return MHC_EHIP;
+      s.ptr = nullptr;
+      s.bytes = 0;
+    }
+    if (hipMalloc(&s.ptr, want) != hipSuccess) {
+      s.ptr = nullptr;
+      return MHC_EHIP;
+    }
+    s.bytes = want;
+  }
+  *out = static_cast<float*>(s.ptr);
+  return MHC_OK;
+}
+
+// Split-K plan for the pre chain: token tiles of 16*ntt tokens, G K-ranges of
+// cpr 16-float chunks each.  G and the tile width depend only on (T <= 16) and
+// the shape, never on which tokens a block holds, so a token's result is the
+// same whatever else is in the batch as long as T stays on the same side of 16.
+struct PrePlan {
+  int ntt, G, cpr;
+  size_t part_floats;
+};
+
+PrePlan plan_pre(int T, int S, int H) {
+  const int n = S * H, R = (2 + S) * S, nrt = (R + 15) / 16;
+  const int nchunks = (n + 15) / 16;
+  PrePlan p;
+  p.ntt = T <= 16 ? 1 : (nrt <= 3 ? 4 : 2);
+  const int tiles = (T + 16 * p.ntt - 1) / (16 * p.ntt);
+  int G;
+  if (tiles == 1) {
+    G = nchunks / 8;
+    if (G > 128) G = 128;
+  } else {
+    G = (512 + tiles - 1) / tiles;
+    if (G > 64) G = 64;
+    if (G > nchunks / 32) G = nchunks / 32;
+  }
+  if (G < 1) G = 1;
+  p.cpr = (nchunks + G - 1) / G;
+  p.G = (nchunks + p.cpr - 1) / p.cpr;
+  p.part_floats = (size_t)p.G * T * (R + 1);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mhc_status_string(int status) {
+  switch (status) {
+    case MHC_OK: return "ok";
+    case MHC_EINVAL: return "invalid argument (size, count, eps, iterations or NULL pointer)";
+    case MHC_EALIGN: return "misaligned: hidden must be a multiple of 4 and pointers 16-byte aligned";
+    case MHC_EUNSUPPORTED: return "unsupported shape (streams > 8 or T*streams*hidden >= 2^31)";
+    case MHC_EHIP: return "HIP runtime error";
+    case MHC_EOVERLAP: return "an output buffer overlaps an input or another output";
+    default: return "unknown status";
+  }
+}
+
+int mhc_site_pre_check(const float* x, const float* fn_w, const float* scale, const float* base,
+                       int T, int streams, int hidden, int iters, float eps, const float* pre,
+                       const float* post, const float* comb, const float* y) {
+  int rc = check_shape(T, streams, hidden);
+  if (rc) return rc;
+  if (iters < 1 || !(eps > 0.0f) || !std::isfinite(eps)) return MHC_EINVAL;
+  if (T == 0) return MHC_OK;
+  const void* ptrs[] = {x, fn_w, scale, base, pre, post, comb, y};
+  for (const void* p : ptrs)
+    if (!p) return MHC_EINVAL;
+  for (const void* p : ptrs)
+    if ((rc = check_ptr(p))) return rc;
+  const size_t S = streams, H = hidden, Tz = T, R = (2 + S) * S;
+  const Span in[] = {span(x, Tz * S * H * 4), span(fn_w, R * S * H * 4), span(scale, 12),
+                     span(base, R * 4)};
+  const Span out[] = {span(pre, Tz * S * 4), span(post, Tz * S * 4), span(comb, Tz * S * S * 4),
+                      span(y, Tz * H * 4)};
+  for (int o = 0; o < 4; ++o) {
+    for (const Span& i : in)
+      if (overlaps(out[o], i)) return MHC_EOVERLAP;
+    for (int p = o + 1; p < 4; ++p)
+      if (overlaps(out[o], out[p])) return MHC_EOVERLAP;
+  }
+  return MHC_OK;
+}
+
+int mhc_site_post_check(const float* x, const float* f, const float* post, const float* comb,
+                        int T, int streams, int hidden, const float* x_out) {
+  int rc = check_shape(T, streams, hidden);
+  if (rc) return rc;
+  if (T == 0) return MHC_OK;
+  const void* ptrs[] = {x, f, post, comb, x_out};
+  for (const void* p : ptrs)
+    if (!p) return MHC_EINVAL;
+  for (const void* p : ptrs)
+    if ((rc = check_ptr(p))) return rc;
+  const size_t S = streams, H = hidden, Tz = T;
+  const Span o = span(x_out, Tz * S * H * 4);
+  const Span in[] = {span(x, Tz * S * H * 4), span(f, Tz * H * 4), span(post, Tz * S * 4),
+                     span(comb, Tz * S * S * 4)};
+  for (const Span& i : in)
+    if (overlaps(o, i)) return MHC_EOVERLAP;
+  return MHC_OK;
+}
+
+int mhc_site_pre(const float* x, const float* fn_w, const float* scale, const float* base, int T,
+                 int streams, int hidden, int iters, float eps, float* pre, float* post,
+                 float* comb, float* y, void* stream) {
+  int rc = mhc_site_pre_check(x, fn_w, scale, base, T, streams, hidden, iters, eps, pre, post,
+                              comb, y);
+  if (rc || T == 0) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int S = streams, H = hidden, n = S * H, R = (2 + S) * S;
+  const PrePlan p = plan_pre(T, S, H);
+  float* part = nullptr;
+  if ((rc = get_scratch(p.part_floats * sizeof(float), &part))) return rc;
+  if (mhc::launch_partials(x, fn_w, T, n, R, p.ntt, p.G, p.cpr, part, st) != hipSuccess)
+    return MHC_EHIP;
+  if (mhc::launch_finish(x, part, p.G, T, S, H, scale, base, iters, eps, pre, post, comb, y,
+                         st) != hipSuccess)
+    return MHC_EHIP;
+  return MHC_OK;
+}
+
+int mhc_site_post(const float* x, const float* f, const float* post, const float* comb, int T,
+                  int streams, int hidden, float* x_out, void* stream) {
+  int rc = mhc_site_post_check(x, f, post, comb, T, streams, hidden, x_out);
+  if (rc || T == 0) return rc;
+  if (mhc::launch_post(x, f, post, comb, T, streams, hidden, x_out,
+                       static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MHC_EHIP;
+  return MHC_OK;
+}
+
+}  // extern "C"

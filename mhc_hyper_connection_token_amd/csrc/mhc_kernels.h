@@ -1,0 +1,21 @@
+// mhc_kernels.h -- host-side launchers of the gfx950 kernels (internal to libmhc).
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace mhc {
+
+// Split-K partial mixes + sums of squares: part[G][T][R+1].
+// ntt = token tiles of 16 per block (1, 2 or 4, depending on the row-tile count).
+hipError_t launch_partials(const float* x, const float* fn_w, int T, int n, int R, int ntt,
+                           int G, int chunks_per_range, float* part, hipStream_t st);
+
+// Reduce partials, gates, Sinkhorn, collapse.
+hipError_t launch_finish(const float* x, const float* part, int G, int T, int S, int H,
+                         const float* scale, const float* base, int iters, float eps,
+                         float* pre, float* post, float* comb, float* y, hipStream_t st);
+
+// Post mix.
+hipError_t launch_post(const float* x, const float* f, const float* post, const float* comb,
+                       int T, int S, int H, float* x_out, hipStream_t st);
+
+}  // namespace mhc

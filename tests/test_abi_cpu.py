@@ -1,0 +1,124 @@
+"""CPU-side checks of the C ABI: the library loads, exports every entry point the
+public header declares, and its host-side argument checks return the documented
+codes.  No GPU work is issued (the *_check entry points make no HIP call)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import mhc_hyper_connection_token_amd as mhc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mhc.h")
+
+OK, EINVAL, EALIGN, EUNSUP, EHIP, EOVERLAP = range(6)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mhc.LIB_PATH):
+        pytest.skip("libmhc.so not built")
+    return mhc.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(mhc_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_two_site_calls():
+    names = declared_functions()
+    assert "mhc_site_pre" in names and "mhc_site_post" in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", mhc.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(mhc_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        getattr(lib, name)  # resolvable through the loader too
+    assert set(mhc.EXPORTED_SYMBOLS) <= exported
+
+
+def test_status_strings(lib):
+    for rc in range(6):
+        assert lib.mhc_status_string(rc)
+    assert lib.mhc_status_string(99) == b"unknown status"
+
+
+# fake, 16-byte aligned, non-overlapping "device" addresses (never dereferenced)
+def _addrs(T, S, H):
+    R = (2 + S) * S
+    sizes = [T * S * H, R * S * H, 4, R, T * S, T * S, T * S * S, T * H]
+    out, a = [], 1 << 30
+    for n in sizes:
+        out.append(a)
+        a += ((n * 4 + 255) // 256) * 256 + 256
+    return out
+
+
+def _pre_check(lib, T=4, S=4, H=128, iters=20, eps=1e-6, addrs=None):
+    a = addrs or _addrs(T, S, H)
+    return lib.mhc_site_pre_check(a[0], a[1], a[2], a[3], T, S, H, iters, eps,
+                                  a[4], a[5], a[6], a[7])
+
+
+def test_pre_check_accepts_the_workloads(lib):
+    for T, S, H in ((4, 4, 128), (1, 4, 4096), (4096, 4, 4096), (1024, 8, 7168), (1, 1, 4)):
+        assert _pre_check(lib, T, S, H) == OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), EINVAL), (dict(S=0), EINVAL), (dict(S=9), EUNSUP), (dict(H=0), EINVAL),
+    (dict(H=130), EALIGN), (dict(iters=0), EINVAL), (dict(eps=0.0), EINVAL),
+    (dict(eps=-1e-6), EINVAL), (dict(eps=float("inf")), EINVAL), (dict(eps=float("nan")), EINVAL),
+    (dict(T=1 << 20, S=8, H=4096), EUNSUP),
+])
+def test_pre_check_refuses(lib, kw, code):
+    args = dict(T=4, S=4, H=128)
+    args.update(kw)
+    assert _pre_check(lib, **args) == code
+
+
+def test_pre_check_pointers(lib):
+    T, S, H = 4, 4, 128
+    a = _addrs(T, S, H)
+    for i in range(8):
+        b = list(a)
+        b[i] = 0
+        assert _pre_check(lib, T, S, H, addrs=b) == EINVAL
+        b[i] = a[i] + 4
+        assert _pre_check(lib, T, S, H, addrs=b) == EALIGN
+    b = list(a)
+    b[7] = a[0]  # y aliases x
+    assert _pre_check(lib, T, S, H, addrs=b) == EOVERLAP
+    b = list(a)
+    b[5] = a[4] + 16  # post overlaps pre
+    assert _pre_check(lib, T, S, H, addrs=b) == EOVERLAP
+    # T == 0 is a no-op whatever the pointers
+    assert lib.mhc_site_pre_check(None, None, None, None, 0, 4, 128, 20, 1e-6,
+                                  None, None, None, None) == OK
+
+
+def test_post_check(lib):
+    T, S, H = 4, 4, 128
+    a = [1 << 30, (1 << 30) + (1 << 20), (1 << 30) + (2 << 20), (1 << 30) + (3 << 20),
+         (1 << 30) + (4 << 20)]
+    assert lib.mhc_site_post_check(*a[:4], T, S, H, a[4]) == OK
+    assert lib.mhc_site_post_check(*a[:4], T, S, H, a[0]) == EOVERLAP
+    assert lib.mhc_site_post_check(*a[:4], T, S, 6, a[4]) == EALIGN
+    assert lib.mhc_site_post_check(*a[:4], T, 0, H, a[4]) == EINVAL
+    assert lib.mhc_site_post_check(None, *a[1:4], T, S, H, a[4]) == EINVAL
+    assert lib.mhc_site_post_check(None, None, None, None, 0, S, H, None) == OK
+
+
+def test_invalid_call_returns_before_any_gpu_work(lib):
+    """The compute entry points refuse bad arguments on the host, so this is safe
+    without a GPU: nothing is enqueued."""
+    assert lib.mhc_site_pre(None, None, None, None, 4, 4, 128, 0, 1e-6,
+                            None, None, None, None, None) == EINVAL
+    assert lib.mhc_site_post(None, None, None, None, 4, 9, 128, None, None) == EUNSUP

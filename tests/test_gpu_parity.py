@@ -1,0 +1,226 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Every case prints what it runs before touching the GPU, so a failing run names
+its case.  Tolerances are in tests/parity.py.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from mhc_inputs import CONFIGS, make_random_shape, make_site
+from parity import (assert_gates_close, assert_streams_close, gate_violation, relative,
+                    STREAM_REL)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module")
+def mhc():
+    _need_gpu()
+    import mhc_hyper_connection_token_amd as m
+    m.load_library()
+    return m
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def _run_pre(mhc, d, iters, eps):
+    out = mhc.site_pre(_dev(d["x"]), _dev(d["fn_w"]), _dev(d["scale"]), _dev(d["base"]),
+                       iters, eps)
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() for o in out]
+
+
+def _run_post(mhc, x, f, post, comb):
+    out = mhc.site_post(_dev(x), _dev(f), _dev(post), _dev(comb))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _check_site(mhc, d, iters, eps, tokens=None, label=""):
+    """Full pre + post parity.  `tokens` limits the oracle to a sample of token rows."""
+    pre, post, comb, y = _run_pre(mhc, d, iters, eps)
+    xo = _run_post(mhc, d["x"], d["f"], post, comb)
+    idx = np.arange(d["x"].shape[0]) if tokens is None else np.asarray(tokens)
+    eps32 = float(np.float32(eps))
+    o = oracle.site_pre(d["x"][idx], d["fn_w"], d["scale"], d["base"], iters, eps32)
+    assert_gates_close(pre[idx], o["pre"], f"{label} pre")
+    assert_gates_close(post[idx], o["post"], f"{label} post")
+    assert_gates_close(comb[idx], o["comb"], f"{label} comb")
+    assert_streams_close(y[idx], o["y"], f"{label} y")
+    # post parity on the GPU's own gates (post and comb taken as given)
+    op = oracle.site_post(d["x"][idx], d["f"][idx], post[idx], comb[idx])
+    assert_streams_close(xo[idx], op, f"{label} x_out")
+    return pre, post, comb, y, xo
+
+
+# ------------------------------------------------------------------ the five workloads
+@pytest.mark.parametrize("name", ["tiny", "decode", "verify4", "verify8"])
+def test_config_parity_full(mhc, name):
+    c = CONFIGS[name]
+    _say(f"config {name} T={c.T} S={c.S} H={c.H}")
+    d = make_site(c)
+    _check_site(mhc, d, c.iters, c.eps, label=name)
+
+
+def _sample_tokens(T, seed=0):
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 15, 16, 17, 31, 32, 63, 64, 127, 128, T // 2, T - 2, T - 1]
+    pick = rng.choice(T, size=min(T, 40), replace=False)
+    return np.unique(np.clip(np.concatenate([fixed, pick]), 0, T - 1))
+
+
+@pytest.mark.parametrize("name", ["prefill", "wide"])
+def test_config_parity_full_size_sampled(mhc, name):
+    c = CONFIGS[name]
+    _say(f"config {name} T={c.T} S={c.S} H={c.H} (sampled tokens)")
+    d = make_site(c)
+    _check_site(mhc, d, c.iters, c.eps, tokens=_sample_tokens(c.T), label=name)
+
+
+# ------------------------------------------------------------------ ragged and edge shapes
+@pytest.mark.parametrize("T,S,H,iters", [
+    (1, 1, 4, 1), (2, 2, 8, 3), (3, 3, 12, 20), (5, 4, 132, 20), (16, 4, 4096, 20),
+    (17, 4, 260, 7), (33, 5, 36, 20), (70, 6, 52, 20), (19, 7, 1028, 20),
+    (9, 8, 7168, 20), (130, 8, 40, 20), (257, 2, 1000, 20), (40, 1, 8196, 50),
+])
+def test_ragged_shapes(mhc, T, S, H, iters):
+    _say(f"ragged T={T} S={S} H={H} iters={iters}")
+    d = make_random_shape(T, S, H, seed=T * 7 + S)
+    _check_site(mhc, d, iters, 1e-6, label=f"T{T}S{S}H{H}")
+
+
+def test_zero_tokens_is_a_no_op(mhc):
+    _say("T=0")
+    x = torch.empty((0, 4, 64), device="cuda")
+    w = torch.zeros((24, 256), device="cuda")
+    out = mhc.site_pre(x, w, torch.ones(3, device="cuda"), torch.zeros(24, device="cuda"), 20, 1e-6)
+    assert out[3].shape == (0, 64)
+    xo = mhc.site_post(x, torch.empty((0, 64), device="cuda"), out[1], out[2])
+    torch.cuda.synchronize()
+    assert xo.shape == (0, 4, 64)
+
+
+def test_many_iterations_and_larger_eps(mhc):
+    c = CONFIGS["tiny"]
+    d = make_site(c)
+    for iters, eps in ((1, 1e-6), (200, 1e-6), (20, 1e-3)):
+        _say(f"tiny iters={iters} eps={eps}")
+        _check_site(mhc, d, iters, eps, label=f"iters{iters}")
+
+
+# ------------------------------------------------------------------ exact special cases
+def test_one_hot_pre_returns_the_stream_bit_exact(mhc):
+    c = CONFIGS["verify4"]
+    d = make_site(c)
+    S = c.S
+    for chosen in range(S):
+        _say(f"one-hot pre stream {chosen}")
+        w = d["fn_w"].copy()
+        w[:S] = 0.0
+        base = d["base"].copy()
+        base[:S] = -1000.0
+        base[chosen] = 1000.0
+        pre, post, comb, y = _run_pre(mhc, dict(d, fn_w=w, base=base), c.iters, c.eps)
+        assert np.array_equal(pre, np.eye(S, dtype=np.float32)[chosen][None].repeat(c.T, 0))
+        assert np.array_equal(y, d["x"][:, chosen, :])
+
+
+def test_identity_post_is_bit_exact(mhc):
+    c = CONFIGS["verify8"]
+    d = make_site(c)
+    _say("post = 0, comb = I")
+    post = np.zeros((c.T, c.S), np.float32)
+    comb = np.broadcast_to(np.eye(c.S, dtype=np.float32), (c.T, c.S, c.S)).copy()
+    xo = _run_post(mhc, d["x"], d["f"], post, comb)
+    assert np.array_equal(xo, d["x"])
+
+
+def test_permutation_post_routes_source_to_target(mhc):
+    S, H, T = 8, 512, 3
+    d = make_random_shape(T, S, H, 77)
+    _say("post permutation")
+    comb = np.zeros((T, S, S), np.float32)
+    for j in range(S):
+        comb[:, j, (j + 3) % S] = 1.0
+    xo = _run_post(mhc, d["x"], d["f"], np.zeros((T, S), np.float32), comb)
+    for k in range(S):
+        assert np.array_equal(xo[:, k], d["x"][:, (k - 3) % S])
+
+
+def test_uniform_comb_block_entries_are_identical(mhc):
+    c = CONFIGS["decode"]
+    d = make_site(c)
+    S, eps, iters = c.S, 0.05, 7
+    _say("uniform comb logits")
+    w = d["fn_w"].copy()
+    w[2 * S:] = 0.0
+    base = d["base"].copy()
+    base[2 * S:] = 0.3
+    pre, post, comb, y = _run_pre(mhc, dict(d, fn_w=w, base=base), iters, eps)
+    assert np.all(comb == comb.reshape(-1)[0])
+    a = np.exp(np.float64(0.3))
+    for _ in range(2 * iters):
+        a = a / (S * a + np.float32(eps))
+    assert abs(comb.reshape(-1)[0] - a) <= 1e-6 + 1e-5 * a
+
+
+# ------------------------------------------------------------------ determinism, invariance
+def test_run_twice_is_bit_identical(mhc):
+    c = CONFIGS["verify8"]
+    d = make_site(c)
+    _say("determinism")
+    a = _run_pre(mhc, d, c.iters, c.eps)
+    b = _run_pre(mhc, d, c.iters, c.eps)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_small_batch_rows_equal_solo_decode_bit_exact(mhc):
+    c = CONFIGS["verify8"]
+    d = make_site(c)
+    _say("T-invariance within the small-batch plan")
+    batch = _run_pre(mhc, d, c.iters, c.eps)
+    for t in (0, 3, 7):
+        solo = _run_pre(mhc, dict(d, x=d["x"][t:t + 1]), c.iters, c.eps)
+        for u, v in zip(batch, solo):
+            assert np.array_equal(u[t], v[0])
+
+
+def test_end_to_end_post_from_oracle_gates(mhc):
+    c = CONFIGS["verify4"]
+    d = make_site(c)
+    _say("post from oracle gates")
+    o = oracle.site_pre(d["x"], d["fn_w"], d["scale"], d["base"], c.iters, float(np.float32(c.eps)))
+    post32 = o["post"].astype(np.float32)
+    comb32 = o["comb"].astype(np.float32)
+    xo = _run_post(mhc, d["x"], d["f"], post32, comb32)
+    assert_streams_close(xo, oracle.site_post(d["x"], d["f"], post32, comb32), "x_out")
+
+
+def test_red_arm_one_iteration_off_is_detected(mhc):
+    """Non-vacuity: an oracle run with one Sinkhorn round fewer must NOT pass."""
+    c = CONFIGS["tiny"]
+    d = make_site(c)
+    _say("red arm")
+    pre, post, comb, y = _run_pre(mhc, d, 3, c.eps)
+    o = oracle.site_pre(d["x"], d["fn_w"], d["scale"], d["base"], 2, float(np.float32(c.eps)))
+    assert gate_violation(comb, o["comb"]) > 0
+
+
+def test_native_library_is_loaded(mhc):
+    maps = open("/proc/self/maps").read()
+    assert mhc.LIB_PATH in maps
