@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of the mHC site program (pre + post) on one MI355X.
+
+A step is one whole site over one batch of synthetic input already resident in
+HBM: mhc_site_pre (mixes, RMS rescale, gates, Sinkhorn, collapse) followed by
+mhc_site_post (post mix).  The timed workload is the prefill chunk (T=4096
+tokens, 4 streams, hidden 4096, 20 Sinkhorn iterations, eps 1e-6): `value` is
+its token throughput.  The same JSON line carries the decode site (T=1) in
+microseconds per site, the HBM roofline of the dominant kernel, and the CPU
+oracle's throughput on the host as a baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       python bench.py --kernels-only N      # a few launches for rocprofv3 runs
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "mHC site tokens/s + HBM GB/s (% peak), streams=4 d=4096; µs/site at T=1"
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill.json")
+
+
+def kernel_source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "mhc_hyper_connection_token_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# kernel -> the source files whose change invalidates its measured traffic
+KERNEL_SOURCES = {
+    "post_kernel": ["mhc_post.hip", "mhc_device.h"],
+    "pre_call": ["mhc_partials.hip", "mhc_finish.hip", "mhc_device.h", "mhc_api.hip"],
+}
+
+
+def algorithmic_bytes(T, S, H):
+    R = (2 + S) * S
+    pre = 4 * (T * (S * H + H + 2 * S + S * S) + R * S * H + 3 + R)
+    post = 4 * T * (2 * S * H + H + S + S * S)
+    return pre, post
+
+
+def to_dev(d, torch):
+    return {k: torch.from_numpy(v).to("cuda") for k, v in d.items()}
+
+
+def alloc_out(T, S, H, torch):
+    e = lambda *s: torch.empty(s, device="cuda", dtype=torch.float32)  # noqa: E731
+    return (e(T, S), e(T, S), e(T, S, S), e(T, H)), e(T, S, H)
+
+
+def run_kernels_only(n, mhc, torch, CONFIGS, make_site):
+    """A handful of launches of each workload kernel plus a plain 256 MiB device
+    copy (the reference for scaling rocprof's byte counters)."""
+    for name in ("prefill", "decode"):
+        c = CONFIGS[name]
+        t = to_dev(make_site(c), torch)
+        (pre_o, xo) = alloc_out(c.T, c.S, c.H, torch)
+        for _ in range(n):
+            mhc.site_pre(t["x"], t["fn_w"], t["scale"], t["base"], c.iters, c.eps, out=pre_o)
+            mhc.site_post(t["x"], t["f"], pre_o[1], pre_o[2], out=xo)
+        torch.cuda.synchronize()
+        print(f"[kernels-only] {name}: {n} sites", flush=True)
+    src = torch.empty(64 << 20, device="cuda", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    for _ in range(n):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("[kernels-only] copy 256 MiB done", flush=True)
+
+
+def time_site(mhc, torch, t, c, out_pre, out_x, steps, warmup):
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        mhc.site_pre(t["x"], t["fn_w"], t["scale"], t["base"], c.iters, c.eps, out=out_pre)
+        mhc.site_post(t["x"], t["f"], out_pre[1], out_pre[2], out=out_x)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        mhc.site_pre(t["x"], t["fn_w"], t["scale"], t["base"], c.iters, c.eps, out=out_pre)
+        ev[i][1].record(stream)
+        mhc.site_post(t["x"], t["f"], out_pre[1], out_pre[2], out=out_x)
+        ev[i][2].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    pre_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    post_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    return total_ms / steps, pre_ms, post_ms, wall
+
+
+def cpu_baseline(c, d, cpu_seconds=15.0, max_wall=30.0):
+    """The fp64 oracle (pre + post) on the host cores over a bounded sample of the
+    prefill workload: whole passes over its tokens (or a prefix, if one pass would
+    exceed the bound), repeated until about `cpu_seconds` of CPU work is done."""
+    import numpy as np
+
+    import oracle
+    threads = oracle.default_threads()
+    eps = float(np.float32(c.eps))
+
+    def one(n):
+        o = oracle.site_pre(d["x"][:n], d["fn_w"], d["scale"], d["base"], c.iters, eps,
+                            nthreads=threads)
+        oracle.site_post(d["x"][:n], d["f"][:n], o["post"].astype(np.float32),
+                         o["comb"].astype(np.float32), nthreads=threads)
+
+    probe = min(c.T, 64)
+    t0 = time.perf_counter()
+    one(probe)
+    per_tok = (time.perf_counter() - t0) / probe
+    n = int(min(c.T, max(probe, (cpu_seconds / threads) / max(per_tok, 1e-9))))
+    passes, tokens, t0 = 0, 0, time.perf_counter()
+    while True:
+        one(n)
+        passes += 1
+        tokens += n
+        dt = time.perf_counter() - t0
+        if dt * threads >= cpu_seconds or dt >= max_wall:
+            break
+    return {"value": round(tokens / dt, 2), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{passes} pass(es) over the first {n} of {c.T} tokens of the prefill "
+                      f"workload, pre + post, {dt:.2f} s wall on {threads} threads"}
+
+
+def load_traffic(kernel):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        rec = json.load(open(TRAFFIC_FILE)).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash(KERNEL_SOURCES[kernel]):
+        return None  # kernel changed since the counters were taken
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-sites", type=int, default=2000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernels-only", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the mHC site program is token-parallel with "
+              "no cross-GPU exchange, and this build runs and reports a single GPU "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mhc_hyper_connection_token_amd as mhc
+    from mhc_inputs import CONFIGS, make_site
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mhc.load_library()
+    if args.kernels_only:
+        run_kernels_only(args.kernels_only, mhc, torch, CONFIGS, make_site)
+        return
+
+    # ---- prefill chunk: the timed workload
+    c = CONFIGS["prefill"]
+    d = make_site(c)
+    t = to_dev(d, torch)
+    out_pre, out_x = alloc_out(c.T, c.S, c.H, torch)
+    ms, pre_ms, post_ms, wall = time_site(mhc, torch, t, c, out_pre, out_x, args.steps,
+                                          args.warmup)
+    pre_b, post_b = algorithmic_bytes(c.T, c.S, c.H)
+    site_gbps = (pre_b + post_b) / (ms * 1e-3) / 1e9
+    if post_ms >= pre_ms:
+        dom, dom_ms, dom_b, bound_name = "post_kernel", post_ms, post_b, "mhc_site_post"
+    else:
+        dom, dom_ms, dom_b, bound_name = "pre_call", pre_ms, pre_b, "mhc_site_pre"
+    achieved = dom_b / (dom_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": bound_name, "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                "traffic": load_traffic(dom), "algorithmic_bytes_per_launch": dom_b,
+                "avg_launch_us": round(dom_ms * 1e3, 2)}
+
+    # ---- decode site (T=1): microseconds per site, back to back
+    cd = CONFIGS["decode"]
+    td = to_dev(make_site(cd), torch)
+    dpre, dx = alloc_out(cd.T, cd.S, cd.H, torch)
+    n = args.decode_sites
+    d_ms, d_pre_ms, d_post_ms, _ = time_site(mhc, torch, td, cd, dpre, dx, n, 100)
+    pre1, post1 = algorithmic_bytes(cd.T, cd.S, cd.H)
+
+    # ---- CPU oracle baseline (host cores, bounded sample)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(c, d)
+
+    line = {
+        "metric": METRIC,
+        "value": round(c.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "prefill chunk: T=4096 tokens, streams=4, hidden=4096, "
+                               "20 Sinkhorn iterations, eps=1e-6 (pre + post per step)",
+                   "T": c.T, "streams": c.S, "hidden": c.H, "iters": c.iters,
+                   "parallelism": "single GPU"},
+        "site_hbm": {"algorithmic_GBps": round(site_gbps, 1),
+                     "frac_of_peak": round(site_gbps / PEAK_HBM_GBPS, 4),
+                     "pre_us": round(pre_ms * 1e3, 2), "post_us": round(post_ms * 1e3, 2),
+                     "algorithmic_bytes_per_step": pre_b + post_b},
+        "decode_t1": {"us_per_site": round(d_ms * 1e3, 3), "pre_us": round(d_pre_ms * 1e3, 3),
+                      "post_us": round(d_post_ms * 1e3, 3), "sites": n,
+                      "note": "HIP-event time per site on the stream, back to back, warm "
+                              "caches; includes inter-kernel gaps",
+                      "algorithmic_bytes_per_site": pre1 + post1},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
