@@ -40,7 +40,8 @@ def kernel_source_hash(names):
 # kernel -> the source files whose change invalidates its measured traffic
 KERNEL_SOURCES = {
     "post_kernel": ["mhc_post.hip", "mhc_device.h"],
-    "pre_call": ["mhc_partials.hip", "mhc_finish.hip", "mhc_device.h", "mhc_api.hip"],
+    "pre_call": ["mhc_fused.hip", "mhc_partials.hip", "mhc_finish.hip", "mhc_decode.hip",
+                 "mhc_split.h", "mhc_device.h", "mhc_api.hip"],
 }
 
 

@@ -37,7 +37,7 @@ def build(verbose: bool = False) -> str:
     noise = "'-packed-fp32-ops' is not a recognized feature"
     msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if ln.strip() and noise not in ln]
     if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs[:60]))
     if verbose and msgs:
         print("\n".join(msgs))
     os.replace(tmp, LIB)

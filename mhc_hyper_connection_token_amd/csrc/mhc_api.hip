@@ -11,6 +11,7 @@ namespace {
 
 constexpr long kMaxElems = 1L << 31;  // T*S*H must stay below this (int indexing)
 constexpr int kMaxTokens = 1 << 23;   // bounds the flattened launch grids
+constexpr int kFusedMinTokens = 128;  // below this the split-K path fills the chip better
 
 int check_ptr(const void* p) {
   if (!p) return MHC_EINVAL;
@@ -35,9 +36,12 @@ int check_shape(int T, int S, int H) {
   return MHC_OK;
 }
 
-// Library-owned scratch, one buffer per device, grown on demand.  Growth waits
-// for the device to go idle before the old buffer is released, so work already
-// enqueued that still reads the old buffer is not disturbed.
+// Library-owned scratch, one buffer per device, grown on demand.  Its first
+// kScratchHeader bytes hold the decode kernel's ticket counter (zeroed when the
+// buffer is allocated; the kernel leaves it at zero); the rest is returned to
+// the caller.  Growth waits for the device to go idle before the old buffer is
+// released, so work already enqueued that still uses it is not disturbed.
+constexpr size_t kScratchHeader = 256;
 struct DeviceScratch {
   void* ptr = nullptr;
   size_t bytes = 0;
@@ -45,13 +49,14 @@ struct DeviceScratch {
 std::mutex g_scratch_mu;
 DeviceScratch g_scratch[64];
 
-int get_scratch(size_t bytes, float** out) {
+int get_scratch(size_t bytes, float** out, unsigned int** counter = nullptr) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MHC_EHIP;
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   DeviceScratch& s = g_scratch[dev];
-  if (s.bytes < bytes) {
-    size_t want = bytes < (size_t(1) << 20) ? (size_t(1) << 20) : bytes + bytes / 4;
+  const size_t need = bytes + kScratchHeader;
+  if (s.bytes < need) {
+    size_t want = need < (size_t(1) << 20) ? (size_t(1) << 20) : need + need / 4;
     if (s.ptr) {
       if (hipDeviceSynchronize() != hipSuccess) return MHC_EHIP;
       if (hipFree(s.ptr) != hipSuccess) return MHC_EHIP;
@@ -62,9 +67,12 @@ int get_scratch(size_t bytes, float** out) {
       s.ptr = nullptr;
       return MHC_EHIP;
     }
+    if (hipMemset(s.ptr, 0, kScratchHeader) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+      return MHC_EHIP;
     s.bytes = want;
   }
-  *out = static_cast<float*>(s.ptr);
+  *out = reinterpret_cast<float*>(static_cast<char*>(s.ptr) + kScratchHeader);
+  if (counter) *counter = static_cast<unsigned int*>(s.ptr);
   return MHC_OK;
 }
 
@@ -168,9 +176,26 @@ int mhc_site_pre(const float* x, const float* fn_w, const float* scale, const fl
   if (rc || T == 0) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int S = streams, H = hidden, n = S * H, R = (2 + S) * S;
+  if (T >= kFusedMinTokens && mhc::fused_supported(S, H)) {
+    // Large batches with a slab that fits on chip: x read once.
+    float* wpack = nullptr;
+    if ((rc = get_scratch(mhc::fused_pack_bytes(S, H), &wpack))) return rc;
+    if (mhc::launch_fused_pre(x, fn_w, scale, base, T, S, H, iters, eps, pre, post, comb, y,
+                              wpack, st) != hipSuccess)
+      return MHC_EHIP;
+    return MHC_OK;
+  }
   const PrePlan p = plan_pre(T, S, H);
   float* part = nullptr;
-  if ((rc = get_scratch(p.part_floats * sizeof(float), &part))) return rc;
+  unsigned int* counter = nullptr;
+  if ((rc = get_scratch(p.part_floats * sizeof(float), &part, &counter))) return rc;
+  if (T <= 2) {
+    // decode sizes: one launch, the last block to finish does the per-token tail
+    if (mhc::launch_decode_pre(x, fn_w, scale, base, T, S, H, iters, eps, p.G, p.cpr, part,
+                               counter, pre, post, comb, y, st) != hipSuccess)
+      return MHC_EHIP;
+    return MHC_OK;
+  }
   if (mhc::launch_partials(x, fn_w, T, n, R, p.ntt, p.G, p.cpr, part, st) != hipSuccess)
     return MHC_EHIP;
   if (mhc::launch_finish(x, part, p.G, T, S, H, scale, base, iters, eps, pre, post, comb, y,

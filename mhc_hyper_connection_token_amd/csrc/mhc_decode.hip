@@ -1,0 +1,125 @@
+// mhc_decode.hip -- the pre chain of one or two tokens in a single launch.
+//
+// Steps (hyper.rs page, module doc: arithmetic contract, lines one to four).
+// At decode sizes the weight (1.5 MiB at 4 x 4096) is the only real traffic,
+// so it is spread over G blocks that each produce split-K partials exactly as
+// the partials kernel does.  Each block then publishes its partials (device-
+// scope release) and takes a ticket from a counter; the block that draws the
+// last ticket adds the partials in the same fixed order as the finish kernel,
+// runs the gates and the one-wavefront Sinkhorn, collapses the streams and
+// resets the counter for the next call.  No block ever waits for another, so
+// the kernel cannot stall on scheduling.  Results are bit-identical to the
+// two-kernel path for the same G.
+#include "mhc_kernels.h"
+#include "mhc_split.h"
+
+namespace mhc {
+
+template <int NRT, int L>
+__global__ __launch_bounds__(256) void decode_pre_kernel(
+    const float* __restrict__ x, const float* __restrict__ fn_w, const float* __restrict__ scale,
+    const float* __restrict__ base, int T, int S, int H, int iters, float eps,
+    int chunks_per_range, float* __restrict__ part, unsigned int* __restrict__ counter,
+    float* __restrict__ pre, float* __restrict__ post, float* __restrict__ comb,
+    float* __restrict__ y) {
+  constexpr int kVals = NRT * 4 + 1;
+  __shared__ float red[4 * kVals * kWave];
+  __shared__ float red256[256];
+  __shared__ float m_raw[2][96];
+  __shared__ float pre_lds[4 * 8];
+  __shared__ int is_last;
+  __shared__ float params[3 + 80];
+
+  const int G = gridDim.x;
+  const int g = blockIdx.x;
+  const int n = S * H, R = (2 + S) * S, RP = R + 1;
+  const int nchunks = (n + 15) >> 4;
+  const int c_beg = g * chunks_per_range;
+  const int c_end = min(nchunks, c_beg + chunks_per_range);
+  stage_site_params(scale, base, R, params);
+
+  // The partials are written with agent-scope (write-through) stores and read
+  // back with agent-scope loads, so no cache write-back or invalidation is
+  // needed: each thread waits until its stores are complete, the block
+  // synchronises, and only then is the ticket drawn.
+  block_partials<NRT, 1, true>(x, fn_w, T, n, R, 0, c_beg, c_end, red,
+                               part + (size_t)g * T * RP);
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0): own stores done
+  __syncthreads();
+  if (threadIdx.x == 0)
+    is_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              (unsigned)(G - 1);
+  __syncthreads();
+  if (!is_last) return;
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // The last block: request the first collapse inputs now, so that their
+  // latency hides behind the reduction and the Sinkhorn.
+  const int HQ = H >> 2;
+  const int total = T * HQ;
+  float4 xq[4][L];
+  auto load_quads = [&](int base_idx) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int idx = base_idx + k * 256;
+      const int ic = idx < total ? idx : threadIdx.x;
+      const int t = ic / HQ, q = ic - t * HQ;
+      const float4* xt = reinterpret_cast<const float4*>(x + (size_t)t * S * H) + q;
+#pragma unroll
+      for (int c = 0; c < L; ++c)
+        if (c < S) xq[k][c] = xt[(size_t)c * HQ];
+    }
+  };
+  load_quads(threadIdx.x);
+
+  for (int t = 0; t < T; ++t)
+    reduce_token_partials<true, 16>(part, G, T, t, RP, red256, m_raw[t]);
+
+  if (L == 4) {
+    if (threadIdx.x < kWave)
+      gates_wave<4>(&m_raw[0][0], 96, T, S, n, params, iters, eps, true, pre, post, comb,
+                    pre_lds);
+  } else {
+    const int t = threadIdx.x >> 6;
+    if (t < T)
+      gates_wave<8>(m_raw[t], 0, 1, S, n, params, iters, eps, true, pre + (size_t)t * S,
+                    post + (size_t)t * S, comb + (size_t)t * S * S, pre_lds + t * 8);
+  }
+  __syncthreads();
+
+  // collapse: y[t, i] = sum_c pre[t, c] * x[t, c, i], four quads per thread in flight
+  for (int base_idx = threadIdx.x; base_idx < total; base_idx += 4 * 256) {
+    if (base_idx != threadIdx.x) load_quads(base_idx);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int idx = base_idx + k * 256;
+      if (idx < total) {
+        const int t = idx / HQ, q = idx - t * HQ;
+        float pc[L];
+#pragma unroll
+        for (int c = 0; c < L; ++c) pc[c] = c < S ? pre_lds[t * 8 + c] : 0.f;
+        reinterpret_cast<float4*>(y + (size_t)t * H)[q] = collapse4<L>(pc, xq[k], S);
+      }
+    }
+  }
+}
+
+hipError_t launch_decode_pre(const float* x, const float* fn_w, const float* scale,
+                             const float* base, int T, int S, int H, int iters, float eps, int G,
+                             int chunks_per_range, float* part, unsigned int* counter,
+                             float* pre, float* post, float* comb, float* y, hipStream_t st) {
+  if (T < 1 || T > 2) return hipErrorInvalidValue;
+  const int R = (2 + S) * S, nrt = (R + 15) / 16;
+#define MHC_D(NR, LL)                                                                          \
+  if (nrt == NR && (S <= 4) == (LL == 4)) {                                                   \
+    hipLaunchKernelGGL((decode_pre_kernel<NR, LL>), dim3(G), dim3(256), 0, st, x, fn_w, scale, \
+                       base, T, S, H, iters, eps, chunks_per_range, part, counter, pre, post,  \
+                       comb, y);                                                               \
+    return hipGetLastError();                                                                  \
+  }
+  MHC_D(1, 4) MHC_D(2, 4) MHC_D(3, 8) MHC_D(4, 8) MHC_D(5, 8)
+#undef MHC_D
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mhc

@@ -1,8 +1,9 @@
 // mhc_device.h -- device-side building blocks shared by the gfx950 kernels.
 //
-// Wavefront-level helpers (64 lanes), the gate epilogue and the one-wavefront
-// Sinkhorn.  The gate forms and Sinkhorn semantics are the ones stated in
-// include/mhc.h (hyper.rs page, module doc: arithmetic contract).
+// Cross-lane sums on DPP and the gfx950 permlane swaps (plain VALU, no LDS),
+// the one-wavefront Sinkhorn, and the gate epilogue.  Gate forms and Sinkhorn
+// semantics are the ones stated in include/mhc.h (hyper.rs page, module doc:
+// arithmetic contract).
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -12,75 +13,203 @@ constexpr int kWave = 64;
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-// Butterfly sum over the lanes whose index differs only in the bits of
-// [lo, hi) (both powers of two).  Every participating lane ends with the same
-// bits: at each level the two partners add the same pair of values.
-template <int LO, int HI>
-__device__ __forceinline__ float xor_sum(float v) {
-#pragma unroll
-  for (int o = LO; o < HI; o <<= 1) v += __shfl_xor(v, o, kWave);
+// ---------------------------------------------------------------- lane exchange
+// DPP move within rows of 16 lanes; CTRL is the DPP control word
+// (quad_perm 0x00-0xFF, row_ror:n 0x120+n, row_half_mirror 0x141).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// v + (the same register of the lane 16 apart within each 32-lane half).  Both
+// lanes of a pair add the same two values in the same order, so they agree to
+// the bit.
+__device__ __forceinline__ float swap16_sum(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// v + (the same register of the lane 32 apart).
+__device__ __forceinline__ float swap32_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Butterfly sums: all lanes of a group end with bit-identical totals.
+__device__ __forceinline__ float sum_xor1_2(float v) {  // over lane bits 0-1
+  v += dpp<0xB1>(v);  // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);  // quad_perm [2,3,0,1]
+  return v;
+}
+__device__ __forceinline__ float sum_xor4_in8(float v) {  // quads of a half-row (bit 2)
+  return v + dpp<0x141>(v);  // row_half_mirror: the other quad of the 8-lane half-row
+}
+__device__ __forceinline__ float sum_xor8_in16(float v) {  // bit 3
+  return v + dpp<0x128>(v);  // row_ror:8 == lane ^ 8 within a row of 16
+}
+
+// Sum over the 16 blocks of a v_mfma_f32_4x4x1_16b_f32 accumulator register
+// (lane 4b + j, b = 0..15): every lane ends with the total of its column j.  The
+// association order differs between lanes, so only one lane per column should
+// be read; it is the same on every run.
+__device__ __forceinline__ float sum_mfma4_blocks(float v) {
+  v += dpp<0x124>(v);  // row_ror:4   (the four quads of a 16-lane row)
+  v += dpp<0x128>(v);  // row_ror:8
+  v = swap16_sum(v);
+  return swap32_sum(v);
+}
+// Sum over each 16-lane row (lane bits 0-3); read one lane per row.
+__device__ __forceinline__ float sum_row16(float v) {
+  v = sum_xor1_2(v);
+  v += dpp<0x124>(v);
+  v += dpp<0x128>(v);
   return v;
 }
 
-__device__ __forceinline__ float sigmoidf_exact_ends(float z) {
-  // 1/(1+exp(-z)): z -> -inf gives exactly 0, z -> +inf exactly 1.
-  return 1.0f / (1.0f + expf(-z));
+// ---------------------------------------------------------------- Sinkhorn
+// Two lane layouts for the S x S block (entries outside S x S hold 0 and stay 0,
+// so padded sums equal the true sums):
+//   L = 4 (S <= 4): lane = 16*j + 4*u + k, four tokens u per wavefront;
+//                   row sums over k = lane bits 0-1, column sums over j = bits 4-5.
+//   L = 8 (S <= 8): lane = 8*j + k, one token per wavefront;
+//                   row sums over bits 0-2, column sums over bits 3-5.
+template <int L>
+__device__ __forceinline__ float row_sum(float v) {
+  v = sum_xor1_2(v);
+  if (L == 8) v = sum_xor4_in8(v);
+  return v;
+}
+template <int L>
+__device__ __forceinline__ float col_sum(float v) {
+  if (L == 8) v = sum_xor8_in16(v);
+  v = swap16_sum(v);
+  return swap32_sum(v);
 }
 
-// Sinkhorn-Knopp on an S x S block held one entry per lane of one wavefront.
-// Lane l holds entry (j = l / P, k = l % P) where P = S rounded up to a power
-// of two (P*P <= 64); entries with j >= S or k >= S, and lanes >= P*P, hold 0
-// and stay 0, so the padded sums equal the true sums.  One iteration = a row
-// pass (sum over k, divide by sum + eps) then a column pass (sum over j).
-template <int P>
-__device__ __forceinline__ float sinkhorn_wave(float c, bool valid, int iters, float eps) {
+// iters rounds of: row pass C /= (row sum + eps), then column pass
+// C /= (column sum + eps).  The division is a hardware reciprocal (1 ulp) and a
+// multiply; zero entries stay zero.
+template <int L>
+__device__ __forceinline__ float sinkhorn_lanes(float c, int iters, float eps) {
   for (int it = 0; it < iters; ++it) {
-    float s = xor_sum<1, P>(c);
-    c = valid ? c / (s + eps) : 0.0f;
-    s = xor_sum<P, P * P>(c);
-    c = valid ? c / (s + eps) : 0.0f;
+    c *= __builtin_amdgcn_rcpf(row_sum<L>(c) + eps);
+    c *= __builtin_amdgcn_rcpf(col_sum<L>(c) + eps);
   }
   return c;
 }
 
-// Gate epilogue for one token, executed by ONE full wavefront (all 64 lanes
-// must call it together).  m_raw[r] = fn_w[r,:] . x[t,:] (unscaled dots) and
-// ss = sum x^2 live in LDS (or any memory visible to the wave).  Writes pre/post
-// (S floats each) and comb (S*S floats, [j][k]) when `write_out` is set, and
-// pre into pre_lds (for the collapse) when pre_lds is non-null.
-template <int P>
-__device__ __forceinline__ void gates_wave(const float* m_raw, float ss, int S, int n,
-                                           const float* __restrict__ scale,
-                                           const float* __restrict__ base, int iters,
-                                           float eps, bool write_out,
-                                           float* __restrict__ pre_out,
-                                           float* __restrict__ post_out,
-                                           float* __restrict__ comb_out, float* pre_lds) {
+// Streaming (non-temporal) 16-byte load / store for data touched exactly once,
+// so that it does not displace reused data (the mixes weight) from L2.
+__device__ __forceinline__ float4 nt_load4(const float* p) {
+  const floatx4 v = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void nt_store4(float* p, float4 v) {
+  __builtin_nontemporal_store(floatx4{v.x, v.y, v.z, v.w}, reinterpret_cast<floatx4*>(p));
+}
+
+__device__ __forceinline__ float sigmoid_exact_ends(float z) {
+  // 1/(1+exp(-z)) with a hardware reciprocal (1 ulp): z -> -inf gives exactly
+  // 0 (rcp(inf) = 0), z -> +inf exactly 1 (rcp(1) = 1), z = 0 exactly 1/2.
+  return __builtin_amdgcn_rcpf(1.0f + expf(-z));
+}
+
+// 1/sqrt(ss/n + eps) with the hardware reciprocal square root (1 ulp).
+__device__ __forceinline__ float rms_inverse(float ss, int n, float eps) {
+  return __builtin_amdgcn_rsqf(ss * (1.0f / (float)n) + eps);
+}
+
+// ---------------------------------------------------------------- gate epilogue
+// The site parameters (scale[3] then base[R]) staged in LDS at kernel start, so
+// that their memory latency is off the path of the gates.  Threads 0 .. R+2 of
+// the block each load one value; a block barrier must follow before use.
+__device__ __forceinline__ void stage_site_params(const float* __restrict__ scale,
+                                                  const float* __restrict__ base, int R,
+                                                  float* params) {
+  const int i = threadIdx.x;
+  if (i < 3)
+    params[i] = scale[i];
+  else if (i < 3 + R)
+    params[i] = base[i - 3];
+}
+
+// Gates of up to NT tokens (NT = 4 for L = 4, 1 for L = 8) in ONE wavefront;
+// all 64 lanes must call it together.
+//   mraw + u*ldm : the unscaled dots fn_w[r,:].x[t,:] (r < R) of token slot u,
+//                  followed at index R by the token's sum of squares.
+//   params       : scale[0..2] then base[0..R-1] (see stage_site_params).
+//   ntok         : valid token slots (the rest are padding).
+//   pre/post/comb: outputs of slot 0 (slot u at + u*S, + u*S, + u*S*S);
+//                  written only when write_out.
+//   pre_lds      : pre gates for the collapse, slot u at + u*8.
+// Per token: rinv = 1/sqrt(ss/n + eps); m = raw*rinv; z = fma(scale_g, m, base);
+// pre = sigmoid(z), post = 2 sigmoid(z), comb = Sinkhorn(exp(z)).
+template <int L>
+__device__ __forceinline__ void gates_wave(const float* mraw, int ldm, int ntok, int S, int n,
+                                           const float* params, int iters, float eps,
+                                           bool write_out, float* __restrict__ pre,
+                                           float* __restrict__ post, float* __restrict__ comb,
+                                           float* pre_lds) {
   const int lane = threadIdx.x & (kWave - 1);
-  const float rinv = 1.0f / sqrtf(ss / (float)n + eps);
-  const float s_pre = scale[0], s_post = scale[1], s_comb = scale[2];
-  // pre / post gates: lanes [0, S) and [S, 2S)
-  if (lane < 2 * S) {
-    const float m = m_raw[lane] * rinv;
-    if (lane < S) {
-      const float g = sigmoidf_exact_ends(fmaf(s_pre, m, base[lane]));
-      if (write_out) pre_out[lane] = g;
-      if (pre_lds) pre_lds[lane] = g;
-    } else {
-      const float g = 2.0f * sigmoidf_exact_ends(fmaf(s_post, m, base[lane]));
-      if (write_out) post_out[lane - S] = g;
+  const int R = (2 + S) * S;
+  const float s_pre = params[0], s_post = params[1], s_comb = params[2];
+  const float* base = params + 3;
+  // pre / post: lane = 8*u + g (g < 2S) for L = 4; lane = g for L = 8
+  {
+    const int u = (L == 4) ? (lane >> 3) : 0;
+    const int g = (L == 4) ? (lane & 7) : lane;
+    if (u < ntok && g < 2 * S && (L == 8 || lane < 32)) {
+      const float* mr = mraw + u * ldm;
+      const float rinv = rms_inverse(mr[R], n, eps);
+      const float m = mr[g] * rinv;
+      if (g < S) {
+        const float v = sigmoid_exact_ends(fmaf(s_pre, m, base[g]));
+        if (write_out) pre[u * S + g] = v;
+        pre_lds[u * 8 + g] = v;
+      } else {
+        const float v = 2.0f * sigmoid_exact_ends(fmaf(s_post, m, base[g]));
+        if (write_out) post[u * S + g - S] = v;
+      }
     }
   }
-  // comb: lane (j, k) with j = lane / P, k = lane % P
-  const int j = lane / P, k = lane % P;
-  const bool valid = (lane < P * P) && (j < S) && (k < S);
+  // comb
+  int j, k, u;
+  if (L == 4) {
+    j = lane >> 4;
+    u = (lane >> 2) & 3;
+    k = lane & 3;
+  } else {
+    j = lane >> 3;
+    u = 0;
+    k = lane & 7;
+  }
+  const bool valid = (j < S) && (k < S) && (u < ntok);
   float c = 0.0f;
   if (valid) {
+    const float* mr = mraw + u * ldm;
+    const float rinv = rms_inverse(mr[R], n, eps);
     const int r = 2 * S + j * S + k;
-    c = expf(fmaf(s_comb, m_raw[r] * rinv, base[r]));
+    c = expf(fmaf(s_comb, mr[r] * rinv, base[r]));
   }
-  c = sinkhorn_wave<P>(c, valid, iters, eps);
-  if (valid && write_out) comb_out[j * S + k] = c;
+  c = sinkhorn_lanes<L>(c, iters, eps);
+  if (valid && write_out) comb[u * S * S + j * S + k] = c;
+}
+
+// y = sum_c pre[c] * x_c, streams in ascending order, first term a product.
+// Shared by every collapse so that all paths agree bit for bit given pre.
+// SMAX is a compile-time bound on S so that xs stays in registers.
+template <int SMAX>
+__device__ __forceinline__ float4 collapse4(const float* pre, const float4* xs, int S) {
+  float4 o = make_float4(pre[0] * xs[0].x, pre[0] * xs[0].y, pre[0] * xs[0].z, pre[0] * xs[0].w);
+#pragma unroll
+  for (int c = 1; c < SMAX; ++c) {
+    if (c < S) {
+      o.x = fmaf(pre[c], xs[c].x, o.x);
+      o.y = fmaf(pre[c], xs[c].y, o.y);
+      o.z = fmaf(pre[c], xs[c].z, o.z);
+      o.w = fmaf(pre[c], xs[c].w, o.w);
+    }
+  }
+  return o;
 }
 
 }  // namespace mhc

@@ -1,0 +1,245 @@
+// mhc_fused.hip -- token-tiled fused pre chain for S <= 4 with the slab held
+// on chip: x is read from HBM exactly once per token.
+//
+// Steps (hyper.rs page, module doc: arithmetic contract, lines one to four):
+// mixes = fn_w . x[t] over the contiguous S*H slab, the sum of squares, the RMS
+// rescale, gates + Sinkhorn, and the collapse y[t,:] = sum_c pre[t,c] x[t,c,:].
+//
+// One block = 512 threads (8 waves) = a tile of 4 consecutive tokens.  Wave w
+// owns the hidden columns [64*w*CPW, 64*(w+1)*CPW) of EVERY stream, so once the
+// gates are known each lane collapses its own registers.
+//
+// Operand traffic.  The contraction runs on v_mfma_f32_4x4x1_16b_f32 (A = 4
+// tokens, B = 4 weight rows, 16 independent blocks = 16 k-streams).  MFMA lane
+// layouts put different rows in neighbouring lanes, which defeats coalescing,
+// so (1) the weight is re-packed once per call into exactly the order the
+// kernel consumes it (every fetch is one contiguous KiB per wave; see
+// pack_weight_kernel), and (2) x is loaded coalesced (16 lanes per token) and
+// moved into the A-operand lanes with ds_bpermute.  Every tile streams the whole
+// packed weight from L2 (1.5 MiB at 4 x 4096), which bounds the kernel by the
+// CU's L1 fill rate; one weight chunk is prefetched ahead of the MFMAs.
+#include "mhc_device.h"
+#include "mhc_device.h"
+#include "mhc_kernels.h"
+
+namespace mhc {
+
+// Weight packing: the operand order the fused kernel consumes.  Entry
+// ((w*NCH + ci)*RG + rg)*64 + lane (a float4) holds, for lane = 4b + j,
+// fn_w[4rg + j][c*H + 64*(w*CPW + u) + 4b .. +3] with c = ci / CPW, u = ci % CPW
+// (zero past the last row or column), so that every weight fetch of the fused
+// kernel is one contiguous kilobyte per wavefront.
+template <int S, int CPW>
+__global__ __launch_bounds__(256) void pack_weight_kernel(const float* __restrict__ fn_w, int H,
+                                                          float4* __restrict__ packed) {
+  constexpr int R = (2 + S) * S;
+  constexpr int RG = (R + 3) / 4;
+  constexpr int NCH = S * CPW;
+  constexpr int TOTAL = 8 * NCH * RG * 64;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= TOTAL) return;
+  const int lane = e & 63;
+  const int rg = (e >> 6) % RG;
+  const int ci = (e / (64 * RG)) % NCH;
+  const int w = e / (64 * RG * NCH);
+  const int b = lane >> 2, j = lane & 3;
+  const int c = ci / CPW, u = ci % CPW;
+  const int row = 4 * rg + j;
+  const int h = 64 * (w * CPW + u) + 4 * b;
+  packed[e] = (row < R && h < H)
+                  ? *reinterpret_cast<const float4*>(fn_w + (size_t)row * S * H + c * H + h)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+template <int S, int CPW, int WD>
+__global__ __launch_bounds__(512) void fused_pre_kernel(
+    const float* __restrict__ x, const float4* __restrict__ wpack,
+    const float* __restrict__ scale, const float* __restrict__ base, int T, int H, int iters,
+    float eps, float* __restrict__ pre, float* __restrict__ post, float* __restrict__ comb,
+    float* __restrict__ y) {
+  constexpr int R = (2 + S) * S;
+  constexpr int RG = (R + 3) / 4;  // weight-row groups of 4
+  constexpr int NW = 8;
+  constexpr int NOUT = 4 * (R + 1);
+  constexpr int NCH = S * CPW;     // chunks per wave: chunk ci = stream ci / CPW, column block ci % CPW
+  __shared__ float red[NW][NOUT];  // per-wave totals, [token][row], row R = sum of squares
+  __shared__ float mr[4][R + 1];
+  __shared__ float pre_lds[4 * 8];
+  __shared__ float params[3 + R];
+
+  stage_site_params(scale, base, R, params);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 4;
+  const int n = S * H;
+  // Memory layout of a lane: token tq = lane / 16, column offset 4 * (lane % 16),
+  // so 16 neighbouring lanes read 256 contiguous bytes of one token.
+  const int tq = lane >> 4, bq = lane & 15;
+  const int tok = t0 + tq;
+  const bool tok_ok = tok < T;
+  const float* xt = x + (size_t)(tok_ok ? tok : 0) * n;
+  // MFMA layout of a lane: block b = lane / 4, token (A row) q = lane % 4.  Its
+  // operand lives in lane 16*q + b of the memory layout.
+  const int src_lane4 = 4 * (16 * (lane & 3) + (lane >> 2));
+
+  float4 xr[NCH];
+  float4 wb[WD + 1][RG];
+  // x is read exactly once: non-temporal, so it does not displace the weight.
+  // The loads are branch-free, which keeps them in issue order so that chunk ci
+  // waits only for itself: a lane past the hidden size reads column 0 instead
+  // (its MFMA terms vanish against the zero-padded packed weight, its square is
+  // masked below, and it stores nothing); lanes of tokens past T read token 0
+  // and are never written out.
+  auto load_x = [&](int ci) {
+    const int c = ci / CPW, u = ci % CPW;
+    const int h = 64 * (wave * CPW + u) + 4 * bq;
+    xr[ci] = nt_load4(xt + c * H + (h < H ? h : 0));
+  };
+  const float4* wp = wpack + (size_t)wave * NCH * RG * 64 + lane;
+  auto load_w = [&](int ci, float4* dst) {
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) dst[rg] = wp[(ci * RG + rg) * 64];
+  };
+
+  floatx4 acc[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) acc[rg] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+#pragma unroll
+  for (int ci = 0; ci < NCH; ++ci) load_x(ci);
+#pragma unroll
+  for (int ci = 0; ci < WD && ci < NCH; ++ci) load_w(ci, wb[ci]);
+#pragma unroll
+  for (int ci = 0; ci < NCH; ++ci) {
+    if (ci + WD < NCH) load_w(ci + WD, wb[(ci + WD) % (WD + 1)]);
+    // keep the prefetch above the compute of this chunk
+    __builtin_amdgcn_sched_barrier(0);
+    const float4 v = xr[ci];
+    if (64 * (wave * CPW + ci % CPW) + 4 * bq < H) {
+      ss = fmaf(v.x, v.x, ss);
+      ss = fmaf(v.y, v.y, ss);
+      ss = fmaf(v.z, v.z, ss);
+      ss = fmaf(v.w, v.w, ss);
+    }
+    // re-lay the chunk into the MFMA A-operand lanes (an opaque copy of the
+    // address keeps each permute inside its own chunk)
+    int sl = src_lane4;
+    asm volatile("" : "+v"(sl));
+    const float ax = __int_as_float(__builtin_amdgcn_ds_bpermute(sl, __float_as_int(v.x)));
+    const float ay = __int_as_float(__builtin_amdgcn_ds_bpermute(sl, __float_as_int(v.y)));
+    const float az = __int_as_float(__builtin_amdgcn_ds_bpermute(sl, __float_as_int(v.z)));
+    const float aw = __int_as_float(__builtin_amdgcn_ds_bpermute(sl, __float_as_int(v.w)));
+    const float4* w = wb[ci % (WD + 1)];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+      acc[rg] = __builtin_amdgcn_mfma_f32_4x4x1f32(ax, w[rg].x, acc[rg], 0, 0, 0);
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+      acc[rg] = __builtin_amdgcn_mfma_f32_4x4x1f32(ay, w[rg].y, acc[rg], 0, 0, 0);
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+      acc[rg] = __builtin_amdgcn_mfma_f32_4x4x1f32(az, w[rg].z, acc[rg], 0, 0, 0);
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+      acc[rg] = __builtin_amdgcn_mfma_f32_4x4x1f32(aw, w[rg].w, acc[rg], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- fixed-order reduction: the 16 MFMA blocks in registers (DPP / permlane),
+  // then the 8 waves in wave order through LDS.
+  // acc[rg][v] at lane (b, j) = partial of (token v, row 4rg + j) over block b;
+  // ss at lane (tq, bq) = partial sum of squares of token tq.
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float t = sum_mfma4_blocks(acc[rg][v]);
+      if (lane < 4 && 4 * rg + lane < R) red[wave][v * (R + 1) + 4 * rg + lane] = t;
+    }
+  {
+    const float t = sum_row16(ss);
+    if ((lane & 15) == 0) red[wave][tq * (R + 1) + R] = t;
+  }
+  __syncthreads();
+  if (threadIdx.x < NOUT) {
+    const int o = threadIdx.x;
+    float sum = red[0][o];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) sum += red[ww][o];
+    mr[o / (R + 1)][o % (R + 1)] = sum;
+  }
+  __syncthreads();
+
+  // ---- gates + Sinkhorn of the four tokens in wave 0
+  if (wave == 0) {
+    const int ntok = min(4, T - t0);
+    gates_wave<4>(&mr[0][0], R + 1, ntok, S, n, params, iters, eps, true,
+                  pre + (size_t)t0 * S, post + (size_t)t0 * S, comb + (size_t)t0 * S * S,
+                  pre_lds);
+  }
+  __syncthreads();
+
+  // ---- collapse from registers (memory layout: token tq, columns 4*bq..)
+  if (tok_ok) {
+    float pc[S];
+#pragma unroll
+    for (int c = 0; c < S; ++c) pc[c] = pre_lds[tq * 8 + c];
+    float* yt = y + (size_t)tok * H;
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      const int h = 64 * (wave * CPW + u) + 4 * bq;
+      if (h < H) {
+        float4 xs[S];
+#pragma unroll
+        for (int c = 0; c < S; ++c) xs[c] = xr[c * CPW + u];
+        nt_store4(yt + h, collapse4<S>(pc, xs, S));
+      }
+    }
+  }
+}
+
+// Chunks per wave for a hidden size: ceil(H / 64 / 8), rounded up to a supported value.
+static int fused_cpw(int H) {
+  const int need = (H + 64 * 8 - 1) / (64 * 8);
+  int cpw = 1;
+  while (cpw < need) cpw *= 2;
+  return cpw;
+}
+
+bool fused_supported(int S, int H) {
+  if (S < 1 || S > 4) return false;
+  const int cpw = fused_cpw(H);
+  return cpw <= 16 && S * cpw <= 32;
+}
+
+size_t fused_pack_bytes(int S, int H) {
+  const int R = (2 + S) * S, RG = (R + 3) / 4;
+  return (size_t)8 * S * fused_cpw(H) * RG * 64 * sizeof(float4);
+}
+
+hipError_t launch_fused_pre(const float* x, const float* fn_w, const float* scale,
+                            const float* base, int T, int S, int H, int iters, float eps,
+                            float* pre, float* post, float* comb, float* y, float* wpack,
+                            hipStream_t st) {
+  if (!fused_supported(S, H)) return hipErrorInvalidValue;
+  const int cpw = fused_cpw(H);
+  const int total = (int)(fused_pack_bytes(S, H) / sizeof(float4));
+  float4* pk = reinterpret_cast<float4*>(wpack);
+  dim3 grid((T + 3) / 4);
+#define MHC_FU(SS, CC)                                                                        \
+  if (S == SS && cpw == CC) {                                                                 \
+    hipLaunchKernelGGL((pack_weight_kernel<SS, CC>), dim3((total + 255) / 256), dim3(256), 0, \
+                       st, fn_w, H, pk);                                                      \
+    hipLaunchKernelGGL((fused_pre_kernel<SS, CC, 1>), grid, dim3(512), 0, st, x, pk, scale,      \
+                       base, T, H, iters, eps, pre, post, comb, y);                           \
+    return hipGetLastError();                                                                 \
+  }
+  MHC_FU(1, 1) MHC_FU(1, 2) MHC_FU(1, 4) MHC_FU(1, 8) MHC_FU(1, 16)
+  MHC_FU(2, 1) MHC_FU(2, 2) MHC_FU(2, 4) MHC_FU(2, 8) MHC_FU(2, 16)
+  MHC_FU(3, 1) MHC_FU(3, 2) MHC_FU(3, 4) MHC_FU(3, 8)
+  MHC_FU(4, 1) MHC_FU(4, 2) MHC_FU(4, 4) MHC_FU(4, 8)
+#undef MHC_FU
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mhc

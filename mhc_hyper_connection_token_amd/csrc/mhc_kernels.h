@@ -14,6 +14,24 @@ hipError_t launch_finish(const float* x, const float* part, int G, int T, int S,
                          const float* scale, const float* base, int iters, float eps,
                          float* pre, float* post, float* comb, float* y, hipStream_t st);
 
+// Token-tiled fused pre chain (slab held on chip), for S <= 4 and H up to a
+// register budget; fused_supported() says whether a shape qualifies.
+// wpack: scratch of fused_pack_bytes(S, H) bytes for the weight in operand order.
+bool fused_supported(int S, int H);
+size_t fused_pack_bytes(int S, int H);
+hipError_t launch_fused_pre(const float* x, const float* fn_w, const float* scale,
+                            const float* base, int T, int S, int H, int iters, float eps,
+                            float* pre, float* post, float* comb, float* y, float* wpack,
+                            hipStream_t st);
+
+// Single-launch pre chain for T <= 2: split-K partials into `part`, last block
+// (ticket on `counter`, which must be zero on entry and is zero again on exit)
+// finishes.  Same G / chunks_per_range as the two-kernel path.
+hipError_t launch_decode_pre(const float* x, const float* fn_w, const float* scale,
+                             const float* base, int T, int S, int H, int iters, float eps, int G,
+                             int chunks_per_range, float* part, unsigned int* counter,
+                             float* pre, float* post, float* comb, float* y, hipStream_t st);
+
 // Post mix.
 hipError_t launch_post(const float* x, const float* f, const float* post, const float* comb,
                        int T, int S, int H, float* x_out, hipStream_t st);

@@ -1,0 +1,203 @@
+// mhc_split.h -- device routines of the split-K pre path, shared by the
+// partials, finish and single-launch decode kernels so that all of them add
+// the same numbers in the same order.
+#pragma once
+#include "mhc_device.h"
+
+namespace mhc {
+
+// Per-block split-K partials (hyper.rs page, module doc: arithmetic contract,
+// first two lines): for tokens [tok0, tok0 + 16*NTT) and the 16-float K chunks
+// [c_beg, c_end) of the slab, the partial dots with the R weight rows and the
+// partial sum of squares, written to pg[t*(R+1) + r] (r == R: sum of squares).
+// 256 threads = four waves; wave w takes chunks c_beg + w, c_beg + w + 4, ...;
+// the four wave partials are added in wave order through `red`
+// (4 * (NRT*NTT*4 + NTT) * 64 floats of LDS).
+//
+// The contraction runs on v_mfma_f32_16x16x4_f32 (fp32 operands, exact fp32
+// products, fp32 accumulation): A = weight rows (16 per tile), B = token slabs
+// (16 tokens per tile).  Each lane loads 16 bytes of one weight row and 16
+// bytes of one token slab per chunk; the four floats feed four MFMAs whose
+// k-index is whatever the lanes hold (A and B agree by construction).
+// Plain store, or (COHERENT) an agent-scope relaxed atomic store that is
+// written through to the device-coherent level, for partials that another
+// block reads in the same launch.
+template <bool COHERENT>
+__device__ __forceinline__ void store_partial(float* p, float v) {
+  if (COHERENT)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+template <bool COHERENT>
+__device__ __forceinline__ float load_partial(const float* p) {
+  if (COHERENT) return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return *p;
+}
+
+template <int NRT, int NTT, bool COHERENT = false>
+__device__ __forceinline__ void block_partials(const float* __restrict__ x,
+                                               const float* __restrict__ fn_w, int T, int n,
+                                               int R, int tok0, int c_beg, int c_end,
+                                               float* red, float* __restrict__ pg) {
+  constexpr int kVals = NRT * NTT * 4 + NTT;  // per lane, per wave
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int RP = R + 1;
+
+  floatx4 acc[NRT][NTT];
+  float ss[NTT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) acc[rt][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) ss[tt] = 0.f;
+
+  const int sub = lane & 15;       // row within a row tile / token within a token tile
+  const int kq = (lane >> 4) * 4;  // this lane's 4-float offset inside a 16-float chunk
+
+  // Row and token pointers, clamped to a valid row / token: out-of-range lanes
+  // read valid memory and are zeroed before use.
+  const float* wrow[NRT];
+  bool wvalid[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int r = rt * 16 + sub;
+    wvalid[rt] = r < R;
+    wrow[rt] = fn_w + (size_t)(wvalid[rt] ? r : 0) * n;
+  }
+  const float* xrow[NTT];
+  bool xvalid[NTT];
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) {
+    const int t = tok0 + tt * 16 + sub;
+    xvalid[tt] = t < T;
+    xrow[tt] = x + (size_t)(xvalid[tt] ? t : 0) * n;
+  }
+
+  // Double-buffered chunk loop: the loads of chunk c + 4 are issued before the
+  // MFMAs of chunk c.  Loads are branch-free (clamped addresses) and the
+  // out-of-range lanes are zeroed by a select when the chunk is consumed.
+  auto load_chunk = [&](int c, float4* a, float4* b) {
+    const int k = c * 16 + kq;
+    const int kc = k < n ? k : 0;
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) a[rt] = *reinterpret_cast<const float4*>(wrow[rt] + kc);
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) b[tt] = *reinterpret_cast<const float4*>(xrow[tt] + kc);
+  };
+  auto sel = [](bool ok, float4 v) {
+    return make_float4(ok ? v.x : 0.f, ok ? v.y : 0.f, ok ? v.z : 0.f, ok ? v.w : 0.f);
+  };
+  float4 a0[NRT], b0[NTT], a1[NRT], b1[NTT];
+  int c = c_beg + wave;
+  if (c < c_end) load_chunk(c, a0, b0);
+  while (c < c_end) {
+    const int cn = c + 4;
+    if (cn < c_end) load_chunk(cn, a1, b1);
+    const bool kin = c * 16 + kq < n;  // n % 4 == 0: a float4 is fully in or fully out
+    float4 a[NRT], b[NTT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) a[rt] = sel(kin && wvalid[rt], a0[rt]);
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) b[tt] = sel(kin && xvalid[tt], b0[tt]);
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) {
+      ss[tt] = fmaf(b[tt].x, b[tt].x, ss[tt]);
+      ss[tt] = fmaf(b[tt].y, b[tt].y, ss[tt]);
+      ss[tt] = fmaf(b[tt].z, b[tt].z, ss[tt]);
+      ss[tt] = fmaf(b[tt].w, b[tt].w, ss[tt]);
+    }
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) {
+        acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rt].x, b[tt].x, acc[rt][tt], 0, 0, 0);
+        acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rt].y, b[tt].y, acc[rt][tt], 0, 0, 0);
+        acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rt].z, b[tt].z, acc[rt][tt], 0, 0, 0);
+        acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rt].w, b[tt].w, acc[rt][tt], 0, 0, 0);
+      }
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) a0[rt] = a1[rt];
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) b0[tt] = b1[tt];
+    c = cn;
+  }
+
+  // Sum of squares: lanes l, l^16, l^32, l^48 hold the same token's partials.
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) ss[tt] = swap32_sum(swap16_sum(ss[tt]));
+
+  // Stage the wave's partials, then add the four waves in fixed order.
+  {
+    int v = 0;
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[(wave * kVals + v++) * kWave + lane] = acc[rt][tt][e];
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) red[(wave * kVals + v++) * kWave + lane] = ss[tt];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < kVals * kWave; idx += 256) {
+    const int v = idx / kWave, l = idx % kWave;
+    const float s = ((red[(0 * kVals + v) * kWave + l] + red[(1 * kVals + v) * kWave + l]) +
+                     red[(2 * kVals + v) * kWave + l]) +
+                    red[(3 * kVals + v) * kWave + l];
+    if (v < NRT * NTT * 4) {
+      // MFMA D layout: row = 4*(l/16) + e within the row tile, token = l % 16.
+      const int rt = v / (NTT * 4), tt = (v / 4) % NTT, e = v % 4;
+      const int r = rt * 16 + 4 * (l >> 4) + e;
+      const int t = tok0 + tt * 16 + (l & 15);
+      if (r < R && t < T) store_partial<COHERENT>(pg + (size_t)t * RP + r, s);
+    } else {
+      const int tt = v - NRT * NTT * 4;
+      const int t = tok0 + tt * 16 + (l & 15);
+      if (l < 16 && t < T) store_partial<COHERENT>(pg + (size_t)t * RP + R, s);
+    }
+  }
+}
+
+// Fixed-order sum of the G partials of token t into m_out[0..R] (256 threads):
+// thread (r, q), q < Q = 256 / (R+1), adds g = q, q + Q, q + 2Q, ... in that
+// order (eight independent loads in flight per batch); then thread r adds the Q
+// sums in q order.  The order depends only on G and R, not on T.  Ends with a
+// block barrier; m_out is in LDS.
+template <bool COHERENT = false, int BATCH = 8>
+__device__ __forceinline__ void reduce_token_partials(const float* __restrict__ part, int G, int T,
+                                                      int t, int RP, float* red256,
+                                                      float* m_out) {
+  const int Q = 256 / RP;
+  {
+    const int r = threadIdx.x % RP, q = threadIdx.x / RP;
+    float s = 0.f;
+    if (q < Q) {
+      const float* p = part + (size_t)t * RP + r;
+      const size_t gstride = (size_t)T * RP;
+      for (int g0 = q; g0 < G; g0 += BATCH * Q) {
+        float v[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          const int g = g0 + u * Q;
+          v[u] = load_partial<COHERENT>(p + (size_t)(g < G ? g : q) * gstride);
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u)
+          if (g0 + u * Q < G) s += v[u];
+      }
+    }
+    red256[threadIdx.x] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x < RP) {
+    float s = 0.f;
+    for (int q = 0; q < Q; ++q) s += red256[q * RP + threadIdx.x];
+    m_out[threadIdx.x] = s;
+  }
+  __syncthreads();
+}
+
+}  // namespace mhc
