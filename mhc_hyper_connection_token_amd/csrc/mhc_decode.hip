@@ -26,7 +26,6 @@ __global__ __launch_bounds__(256) void decode_pre_kernel(
   __shared__ float red[4 * kVals * kWave];
   __shared__ float red256[256];
   __shared__ float m_raw[2][96];
-  __shared__ float pre_lds[4 * 8];
   __shared__ int is_last;
   __shared__ float params[3 + 80];
 
@@ -53,16 +52,26 @@ __global__ __launch_bounds__(256) void decode_pre_kernel(
   if (!is_last) return;
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-  // The last block: request the first collapse inputs now, so that their
-  // latency hides behind the reduction and the Sinkhorn.
+  // The last block.  All four waves add the partials first (their loads are
+  // the only ones in flight), then the block splits: the Sinkhorn wave(s)
+  // compute post and comb while the other waves compute the pre gates
+  // themselves and collapse, so the two tails overlap.
+  for (int t = 0; t < T; ++t)
+    reduce_token_partials<true, 16>(part, G, T, t, RP, red256, m_raw[t]);
+
+  const int wave = threadIdx.x >> 6;
+  const int sink_waves = (L == 4) ? 1 : T;
+  const int ct = threadIdx.x - kWave * sink_waves;  // collapse thread index (>= 0 in those waves)
+  const int nct = blockDim.x - kWave * sink_waves;
+  constexpr int KB = (L == 4) ? 6 : 3;              // quads in flight per collapse thread
   const int HQ = H >> 2;
   const int total = T * HQ;
-  float4 xq[4][L];
-  auto load_quads = [&](int base_idx) {
+  float4 xq[KB][L];
+  auto load_batch = [&](int i0) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int idx = base_idx + k * 256;
-      const int ic = idx < total ? idx : threadIdx.x;
+    for (int k = 0; k < KB; ++k) {
+      const int idx = i0 + k * nct;
+      const int ic = idx < total ? idx : 0;  // past the end: re-read quad 0, never stored
       const int t = ic / HQ, q = ic - t * HQ;
       const float4* xt = reinterpret_cast<const float4*>(x + (size_t)t * S * H) + q;
 #pragma unroll
@@ -70,35 +79,36 @@ __global__ __launch_bounds__(256) void decode_pre_kernel(
         if (c < S) xq[k][c] = xt[(size_t)c * HQ];
     }
   };
-  load_quads(threadIdx.x);
 
-  for (int t = 0; t < T; ++t)
-    reduce_token_partials<true, 16>(part, G, T, t, RP, red256, m_raw[t]);
-
-  if (L == 4) {
-    if (threadIdx.x < kWave)
-      gates_wave<4>(&m_raw[0][0], 96, T, S, n, params, iters, eps, true, pre, post, comb,
-                    pre_lds);
-  } else {
-    const int t = threadIdx.x >> 6;
-    if (t < T)
-      gates_wave<8>(m_raw[t], 0, 1, S, n, params, iters, eps, true, pre + (size_t)t * S,
-                    post + (size_t)t * S, comb + (size_t)t * S * S, pre_lds + t * 8);
+  if (wave < sink_waves) {
+    if (L == 4)
+      gates_wave<4, false>(&m_raw[0][0], 96, T, S, n, params, iters, eps, true, pre, post, comb,
+                           nullptr);
+    else
+      gates_wave<8, false>(m_raw[wave], 0, 1, S, n, params, iters, eps, true, nullptr,
+                           post + (size_t)wave * S, comb + (size_t)wave * S * S, nullptr);
+    return;
   }
-  __syncthreads();
 
-  // collapse: y[t, i] = sum_c pre[t, c] * x[t, c, i], four quads per thread in flight
-  for (int base_idx = threadIdx.x; base_idx < total; base_idx += 4 * 256) {
-    if (base_idx != threadIdx.x) load_quads(base_idx);
+  // collapse: y[t, i] = sum_c pre[t, c] * x[t, c, i]
+  load_batch(ct);
+  float pc[2][L];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int idx = base_idx + k * 256;
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int c = 0; c < L; ++c)
+      pc[t][c] = (t < T && c < S) ? pre_gate(m_raw[t], c, R, n, eps, params) : 0.f;
+  if (ct < T * S) pre[ct] = pre_gate(m_raw[ct / S], ct % S, R, n, eps, params);
+
+  for (int i0 = ct; i0 < total; i0 += KB * nct) {
+    if (i0 != ct) load_batch(i0);
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int idx = i0 + k * nct;
       if (idx < total) {
         const int t = idx / HQ, q = idx - t * HQ;
-        float pc[L];
-#pragma unroll
-        for (int c = 0; c < L; ++c) pc[c] = c < S ? pre_lds[t * 8 + c] : 0.f;
-        reinterpret_cast<float4*>(y + (size_t)t * H)[q] = collapse4<L>(pc, xq[k], S);
+        reinterpret_cast<float4*>(y + (size_t)t * H)[q] =
+            collapse4<L>(t == 0 ? pc[0] : pc[1], xq[k], S);
       }
     }
   }

@@ -113,9 +113,20 @@ __device__ __forceinline__ float sigmoid_exact_ends(float z) {
   return __builtin_amdgcn_rcpf(1.0f + expf(-z));
 }
 
-// 1/sqrt(ss/n + eps) with the hardware reciprocal square root (1 ulp).
+// 1/sqrt(ss/n + eps) with the hardware reciprocal square root (1 ulp).  The
+// fused multiply-add is explicit so that every caller rounds identically.
 __device__ __forceinline__ float rms_inverse(float ss, int n, float eps) {
-  return __builtin_amdgcn_rsqf(ss * (1.0f / (float)n) + eps);
+  return __builtin_amdgcn_rsqf(fmaf(ss, 1.0f / (float)n, eps));
+}
+
+// The pre gate of stream c of one token: sigmoid(scale_pre * raw_c * rinv + base_c)
+// from the token's unscaled dots mr[0..R) and sum of squares mr[R], with the site
+// parameters as staged by stage_site_params.  Every path that needs a pre gate
+// (the gate epilogue and the collapse) calls this, so they agree to the bit.
+__device__ __forceinline__ float pre_gate(const float* mr, int c, int R, int n, float eps,
+                                          const float* params) {
+  const float rinv = rms_inverse(mr[R], n, eps);
+  return sigmoid_exact_ends(fmaf(params[0], mr[c] * rinv, params[3 + c]));
 }
 
 // ---------------------------------------------------------------- gate epilogue
@@ -133,7 +144,8 @@ __device__ __forceinline__ void stage_site_params(const float* __restrict__ scal
 }
 
 // Gates of up to NT tokens (NT = 4 for L = 4, 1 for L = 8) in ONE wavefront;
-// all 64 lanes must call it together.
+// all 64 lanes must call it together.  With PRE = false the pre gates are left
+// to the caller (pre_gate), and pre / pre_lds are not touched.
 //   mraw + u*ldm : the unscaled dots fn_w[r,:].x[t,:] (r < R) of token slot u,
 //                  followed at index R by the token's sum of squares.
 //   params       : scale[0..2] then base[0..R-1] (see stage_site_params).
@@ -143,7 +155,7 @@ __device__ __forceinline__ void stage_site_params(const float* __restrict__ scal
 //   pre_lds      : pre gates for the collapse, slot u at + u*8.
 // Per token: rinv = 1/sqrt(ss/n + eps); m = raw*rinv; z = fma(scale_g, m, base);
 // pre = sigmoid(z), post = 2 sigmoid(z), comb = Sinkhorn(exp(z)).
-template <int L>
+template <int L, bool PRE = true>
 __device__ __forceinline__ void gates_wave(const float* mraw, int ldm, int ntok, int S, int n,
                                            const float* params, int iters, float eps,
                                            bool write_out, float* __restrict__ pre,
@@ -151,7 +163,7 @@ __device__ __forceinline__ void gates_wave(const float* mraw, int ldm, int ntok,
                                            float* pre_lds) {
   const int lane = threadIdx.x & (kWave - 1);
   const int R = (2 + S) * S;
-  const float s_pre = params[0], s_post = params[1], s_comb = params[2];
+  const float s_post = params[1], s_comb = params[2];
   const float* base = params + 3;
   // pre / post: lane = 8*u + g (g < 2S) for L = 4; lane = g for L = 8
   {
@@ -159,14 +171,15 @@ __device__ __forceinline__ void gates_wave(const float* mraw, int ldm, int ntok,
     const int g = (L == 4) ? (lane & 7) : lane;
     if (u < ntok && g < 2 * S && (L == 8 || lane < 32)) {
       const float* mr = mraw + u * ldm;
-      const float rinv = rms_inverse(mr[R], n, eps);
-      const float m = mr[g] * rinv;
       if (g < S) {
-        const float v = sigmoid_exact_ends(fmaf(s_pre, m, base[g]));
-        if (write_out) pre[u * S + g] = v;
-        pre_lds[u * 8 + g] = v;
+        if (PRE) {
+          const float v = pre_gate(mr, g, R, n, eps, params);
+          if (write_out) pre[u * S + g] = v;
+          pre_lds[u * 8 + g] = v;
+        }
       } else {
-        const float v = 2.0f * sigmoid_exact_ends(fmaf(s_post, m, base[g]));
+        const float rinv = rms_inverse(mr[R], n, eps);
+        const float v = 2.0f * sigmoid_exact_ends(fmaf(s_post, mr[g] * rinv, base[g]));
         if (write_out) post[u * S + g - S] = v;
       }
     }

@@ -7,8 +7,9 @@
 // collapse the streams: y[t,i] = sum_c pre[t,c] * x[t,c,i].
 //
 // Grid: (T, HB).  Block y-index hb covers a contiguous range of hidden quads
-// for the collapse; every block of a token recomputes the (cheap) gates so that
-// no cross-block wait is needed, and only hb == 0 writes pre/post/comb.  The
+// for the collapse; every block of a token recomputes the (cheap) pre gates so
+// that no cross-block wait is needed, and only hb == 0 runs the Sinkhorn and
+// writes pre/post/comb.  The
 // first x quads of the collapse are loaded before the gates are computed, so
 // their latency hides behind the reduction and the Sinkhorn.
 #include "mhc_kernels.h"
@@ -29,7 +30,6 @@ __global__ __launch_bounds__(256) void finish_kernel(
   const int HQ = H >> 2;
   __shared__ float red[256];
   __shared__ float m_raw[96];
-  __shared__ float pre_lds[8];
   __shared__ float params[3 + 80];
   stage_site_params(scale, base, R, params);
 
@@ -48,16 +48,21 @@ __global__ __launch_bounds__(256) void finish_kernel(
   // 1. fixed-order reduction of the G partials
   reduce_token_partials(part, G, T, t, RP, red, m_raw);
 
-  // 2. gates + Sinkhorn in wave 0
-  if (threadIdx.x < kWave)
-    gates_wave<L>(m_raw, 0, 1, S, S * H, params, iters, eps, hb == 0, pre + (size_t)t * S,
-                  post + (size_t)t * S, comb + (size_t)t * S * S, pre_lds);
-  __syncthreads();
-
-  // 3. collapse
+  // 2. pre gates, computed by every thread (uniform); only block hb == 0 runs
+  // the Sinkhorn (wave 0, post and comb) and writes the gates.  No barrier
+  // follows, so the other waves collapse while wave 0 iterates.
   float pc[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) pc[c] = c < S ? pre_lds[c] : 0.f;
+  for (int c = 0; c < 8; ++c) pc[c] = c < S ? pre_gate(m_raw, c, R, S * H, eps, params) : 0.f;
+  if (hb == 0) {
+    if (threadIdx.x < S)
+      pre[(size_t)t * S + threadIdx.x] = pre_gate(m_raw, threadIdx.x, R, S * H, eps, params);
+    if (threadIdx.x < kWave)
+      gates_wave<L, false>(m_raw, 0, 1, S, S * H, params, iters, eps, true, nullptr,
+                           post + (size_t)t * S, comb + (size_t)t * S * S, nullptr);
+  }
+
+  // 3. collapse
   float4* yt = reinterpret_cast<float4*>(y + (size_t)t * H);
   if (qa < q1) yt[qa] = collapse4<8>(pc, xq, S);
   for (int q = qa + 256; q < q1; q += 256) {
