@@ -11,6 +11,7 @@ oracle's throughput on the host as a baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --kernels-only N      # a few launches for rocprofv3 runs
+       python bench.py --write-traffic FETCH_DB WRITE_DB   # counters -> profiles/
 """
 from __future__ import annotations
 
@@ -155,6 +156,64 @@ def load_traffic(kernel):
     return rec.get("bytes_per_launch")
 
 
+# prefill kernels whose counters make up each measured unit
+TRAFFIC_UNITS = {
+    "pre_call": ["pack_weight_kernel", "fused_pre_kernel"],
+    "post_kernel": ["post_kernel"],
+}
+
+
+def write_traffic(fetch_db, write_db):
+    """Turn two rocprofv3 counter runs of `--kernels-only` (FETCH_SIZE, then
+    WRITE_SIZE; KiB per dispatch) into bytes per prefill launch, scaled by what
+    the same counters read for the plain 256 MiB device copy of that run."""
+    import sqlite3
+    import statistics
+    from collections import defaultdict
+
+    def per_kernel(db, counter):
+        rows = sqlite3.connect(db).execute(
+            "select kernel_name, grid_size, counter_name, value from counters_collection"
+        ).fetchall()
+        groups = defaultdict(list)
+        for name, grid, cname, value in rows:
+            if cname == counter:
+                short = name.split("(")[0].split("<")[0].split("::")[-1].strip()
+                groups[(short, int(grid))].append(float(value))
+        return {k: statistics.mean(v) for k, v in groups.items()}
+
+    fetch, write = per_kernel(fetch_db, "FETCH_SIZE"), per_kernel(write_db, "WRITE_SIZE")
+    copy_kib = 256 * 1024.0
+    copies = [k for k in write if "copy" in k[0].lower() and abs(write[k] - copy_kib) < 1024]
+    if not copies or copies[0] not in fetch:
+        raise SystemExit("no 256 MiB copy kernel found in the counter runs")
+    ck = copies[0]
+    f_scale, w_scale = copy_kib / fetch[ck], copy_kib / write[ck]
+
+    def largest(name):  # the prefill launch of a kernel has its largest grid
+        keys = [k for k in fetch if k[0] == name and k in write]
+        if not keys:
+            raise SystemExit(f"kernel {name} missing from the counter runs")
+        return max(keys, key=lambda k: k[1])
+
+    out = {"fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "copy_kernel": ck[0], "copy_fetch_kib": fetch[ck], "copy_write_kib": write[ck]}
+    for unit, names in TRAFFIC_UNITS.items():
+        parts = {}
+        total = 0.0
+        for nm in names:
+            k = largest(nm)
+            b = (f_scale * fetch[k] + w_scale * write[k]) * 1024.0
+            parts[nm] = {"grid_threads": k[1], "fetch_kib": fetch[k], "write_kib": write[k],
+                         "scaled_bytes": round(b)}
+            total += b
+        out[unit] = {"bytes_per_launch": round(total), "kernels": parts,
+                     "source_hash": kernel_source_hash(KERNEL_SOURCES[unit])}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -163,7 +222,12 @@ def main():
     ap.add_argument("--decode-sites", type=int, default=2000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels-only", type=int, default=0)
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="write the measured traffic file from two rocprofv3 counter runs")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the mHC site program is token-parallel with "
               "no cross-GPU exchange, and this build runs and reports a single GPU "
@@ -194,9 +258,10 @@ def main():
     pre_b, post_b = algorithmic_bytes(c.T, c.S, c.H)
     site_gbps = (pre_b + post_b) / (ms * 1e-3) / 1e9
     if post_ms >= pre_ms:
-        dom, dom_ms, dom_b, bound_name = "post_kernel", post_ms, post_b, "mhc_site_post"
+        dom, dom_ms, dom_b, bound_name = "post_kernel", post_ms, post_b, "mhc_site_post (post_kernel)"
     else:
-        dom, dom_ms, dom_b, bound_name = "pre_call", pre_ms, pre_b, "mhc_site_pre"
+        dom, dom_ms, dom_b, bound_name = ("pre_call", pre_ms, pre_b,
+                                          "mhc_site_pre (pack_weight_kernel + fused_pre_kernel)")
     achieved = dom_b / (dom_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": bound_name, "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
