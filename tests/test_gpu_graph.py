@@ -1,0 +1,70 @@
+"""HIP graph capture of whole sites: every replay equals the eager result bit for bit.
+
+Covers the three pre schedules (single-launch decode, split partials + finish,
+packed-weight fused tiles) and the post kernel.  Between replays the program
+runs its own eager work (a different site through the same library scratch)
+and synchronises, so a replay that depended on state left by the capture, or
+on memory cleared only once, would differ.
+"""
+import numpy as np
+import pytest
+
+from mhc_inputs import make_random_shape
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def mhc():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mhc_hyper_connection_token_amd as m
+    m.load_library()
+    return m
+
+
+def _site(mhc, d, iters, eps, out_pre, out_x):
+    mhc.site_pre(d["x"], d["fn_w"], d["scale"], d["base"], iters, eps, out=out_pre)
+    mhc.site_post(d["x"], d["f"], out_pre[1], out_pre[2], out=out_x)
+
+
+def _alloc(T, S, H):
+    e = lambda *s: torch.empty(s, device="cuda", dtype=torch.float32)  # noqa: E731
+    return (e(T, S), e(T, S), e(T, S, S), e(T, H)), e(T, S, H)
+
+
+@pytest.mark.parametrize("T,S,H", [(1, 4, 4096), (2, 8, 512), (8, 4, 4096), (130, 4, 1024)])
+def test_graph_replays_match_eager(mhc, T, S, H):
+    print(f"[case] graph T={T} S={S} H={H}", flush=True)
+    iters, eps = 20, 1e-6
+    d = {k: torch.from_numpy(v).cuda() for k, v in make_random_shape(T, S, H, 5 + T).items()}
+    other = {k: torch.from_numpy(v).cuda()
+             for k, v in make_random_shape(T, S, H, 99 + T).items()}
+    out_pre, out_x = _alloc(T, S, H)
+    o_pre, o_x = _alloc(T, S, H)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        _site(mhc, d, iters, eps, out_pre, out_x)  # eager reference (also sizes the scratch)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in out_pre] + [out_x.clone()]
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        _site(mhc, d, iters, eps, out_pre, out_x)
+    torch.cuda.synchronize()
+
+    for rep in range(3):
+        for t in list(out_pre) + [out_x]:
+            t.fill_(float("nan"))
+        with torch.cuda.stream(s):
+            _site(mhc, other, iters, eps, o_pre, o_x)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = list(out_pre) + [out_x]
+        for name, a, b in zip(("pre", "post", "comb", "y", "x_out"), got, ref):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager result"
