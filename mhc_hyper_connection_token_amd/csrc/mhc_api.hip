@@ -37,10 +37,11 @@ int check_shape(int T, int S, int H) {
 }
 
 // Library-owned scratch, one buffer per device, grown on demand.  Its first
-// kScratchHeader bytes hold the decode kernel's ticket counter (zeroed when the
-// buffer is allocated; the kernel leaves it at zero); the rest is returned to
-// the caller.  Growth waits for the device to go idle before the old buffer is
-// released, so work already enqueued that still uses it is not disturbed.
+// kScratchHeader bytes hold the decode kernels' ticket counter (zeroed when the
+// buffer is allocated; the kernels leave it at zero); the rest is returned to
+// the caller (split-K partials, packed weight).  Growth waits for the device
+// to go idle before the old buffer is released, so work already enqueued that
+// still uses it is not disturbed.
 constexpr size_t kScratchHeader = 256;
 struct DeviceScratch {
   void* ptr = nullptr;
@@ -49,7 +50,12 @@ struct DeviceScratch {
 std::mutex g_scratch_mu;
 DeviceScratch g_scratch[64];
 
-int get_scratch(size_t bytes, float** out, unsigned int** counter = nullptr) {
+struct Scratch {
+  float* general = nullptr;
+  unsigned int* counter = nullptr;
+};
+
+int get_scratch(size_t bytes, Scratch* out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MHC_EHIP;
   std::lock_guard<std::mutex> lock(g_scratch_mu);
@@ -71,8 +77,9 @@ int get_scratch(size_t bytes, float** out, unsigned int** counter = nullptr) {
       return MHC_EHIP;
     s.bytes = want;
   }
-  *out = reinterpret_cast<float*>(static_cast<char*>(s.ptr) + kScratchHeader);
-  if (counter) *counter = static_cast<unsigned int*>(s.ptr);
+  char* base = static_cast<char*>(s.ptr);
+  out->counter = reinterpret_cast<unsigned int*>(base);
+  out->general = reinterpret_cast<float*>(base + kScratchHeader);
   return MHC_OK;
 }
 
@@ -178,23 +185,25 @@ int mhc_site_pre(const float* x, const float* fn_w, const float* scale, const fl
   const int S = streams, H = hidden, n = S * H, R = (2 + S) * S;
   if (T >= kFusedMinTokens && mhc::fused_supported(S, H)) {
     // Large batches with a slab that fits on chip: x read once.
-    float* wpack = nullptr;
-    if ((rc = get_scratch(mhc::fused_pack_bytes(S, H), &wpack))) return rc;
+    Scratch sc;
+    if ((rc = get_scratch(mhc::fused_pack_bytes(S, H), &sc))) return rc;
     if (mhc::launch_fused_pre(x, fn_w, scale, base, T, S, H, iters, eps, pre, post, comb, y,
-                              wpack, st) != hipSuccess)
+                              sc.general, st) != hipSuccess)
       return MHC_EHIP;
     return MHC_OK;
   }
   const PrePlan p = plan_pre(T, S, H);
-  float* part = nullptr;
-  unsigned int* counter = nullptr;
-  if ((rc = get_scratch(p.part_floats * sizeof(float), &part, &counter))) return rc;
+  Scratch sc;
+  if ((rc = get_scratch(p.part_floats * sizeof(float), &sc))) return rc;
+  float* part = sc.general;
   if (T <= 2) {
-    // decode sizes: one launch, the last block to finish does the per-token tail
-    if (mhc::launch_decode_pre(x, fn_w, scale, base, T, S, H, iters, eps, p.G, p.cpr, part,
-                               counter, pre, post, comb, y, st) != hipSuccess)
-      return MHC_EHIP;
-    return MHC_OK;
+    // decode sizes: one launch; the block that draws the last ticket finishes
+    hipError_t e = mhc::decode4_supported(T, S, p.G)
+                       ? mhc::launch_decode4_pre(x, fn_w, scale, base, T, S, H, iters, eps, p.G,
+                                                 p.cpr, part, sc.counter, pre, post, comb, y, st)
+                       : mhc::launch_decode_pre(x, fn_w, scale, base, T, S, H, iters, eps, p.G,
+                                                p.cpr, part, sc.counter, pre, post, comb, y, st);
+    return e == hipSuccess ? MHC_OK : MHC_EHIP;
   }
   if (mhc::launch_partials(x, fn_w, T, n, R, p.ntt, p.G, p.cpr, part, st) != hipSuccess)
     return MHC_EHIP;

@@ -3,13 +3,20 @@
 // Steps (hyper.rs page, module doc: arithmetic contract, lines one to four).
 // At decode sizes the weight (1.5 MiB at 4 x 4096) is the only real traffic,
 // so it is spread over G blocks that each produce split-K partials exactly as
-// the partials kernel does.  Each block then publishes its partials (device-
-// scope release) and takes a ticket from a counter; the block that draws the
-// last ticket adds the partials in the same fixed order as the finish kernel,
-// runs the gates and the one-wavefront Sinkhorn, collapses the streams and
-// resets the counter for the next call.  No block ever waits for another, so
+// the partials kernel does.  Which block finishes (adds the partials in the
+// finish kernel's fixed order, runs the gates and the one-wavefront Sinkhorn,
+// collapses the streams) is decided without any block waiting for another, so
 // the kernel cannot stall on scheduling.  Results are bit-identical to the
 // two-kernel path for the same G.
+//
+// S <= 4 (decode4_pre_kernel): partials, then a ticket counter; the block
+// that draws the last ticket requests every partial and, right behind them,
+// the collapse operands, adds the partials, and then splits: wave 0 runs the
+// gates and the Sinkhorn while the other waves compute the pre gates
+// themselves and collapse.  It resets the counter for the next call.
+//
+// S > 4 (decode_pre_kernel): the same ticket scheme with the 256-thread
+// reduction of the finish kernel.
 #include "mhc_kernels.h"
 #include "mhc_split.h"
 
@@ -41,8 +48,9 @@ __global__ __launch_bounds__(256) void decode_pre_kernel(
   // back with agent-scope loads, so no cache write-back or invalidation is
   // needed: each thread waits until its stores are complete, the block
   // synchronises, and only then is the ticket drawn.
-  block_partials<NRT, 1, true>(x, fn_w, T, n, R, 0, c_beg, c_end, red,
-                               part + (size_t)g * T * RP);
+  float* pg = part + (size_t)g * T * RP;
+  block_partials<NRT, 1>(x, fn_w, T, n, R, 0, c_beg, c_end, red,
+                         [=](size_t i, float v) { store_partial<true>(pg + i, v); });
   __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0): own stores done
   __syncthreads();
   if (threadIdx.x == 0)
@@ -112,6 +120,145 @@ __global__ __launch_bounds__(256) void decode_pre_kernel(
       }
     }
   }
+}
+
+template <int NRT>
+__global__ __launch_bounds__(256) void decode4_pre_kernel(
+    const float* __restrict__ x, const float* __restrict__ fn_w, const float* __restrict__ scale,
+    const float* __restrict__ base, int T, int S, int H, int iters, float eps,
+    int chunks_per_range, float* __restrict__ part, unsigned int* __restrict__ counter,
+    float* __restrict__ pre, float* __restrict__ post, float* __restrict__ comb,
+    float* __restrict__ y) {
+  constexpr int kVals = NRT * 4 + 1;
+  constexpr int KB = 6;  // collapse quads in flight per collapse thread
+  __shared__ float red[4 * kVals * kWave];
+  __shared__ float red256[2][256];
+  __shared__ float m_raw[2][32];
+  __shared__ float params[3 + 24];
+  __shared__ int is_last;
+
+  const int G = gridDim.x;
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n = S * H, R = (2 + S) * S, RP = R + 1;
+  const int nchunks = (n + 15) >> 4;
+  const int c_beg = g * chunks_per_range;
+  const int c_end = min(nchunks, c_beg + chunks_per_range);
+  stage_site_params(scale, base, R, params);
+
+  float* pg = part + (size_t)g * T * RP;
+  block_partials<NRT, 1>(x, fn_w, T, n, R, 0, c_beg, c_end, red,
+                         [=](size_t i, float v) { store_partial<true>(pg + i, v); });
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores are complete ...
+  __syncthreads();                // ... and so are those of the whole block
+  if (tid == 0)
+    is_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              (unsigned)(G - 1);
+  __syncthreads();
+  if (!is_last) return;
+  if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // The last block.  First every partial is requested (thread (r, q) takes
+  // blocks q, q + Q, ... of row r, the order in which the finish kernel adds
+  // them), then the first collapse operands, so that the reduction waits only
+  // for its own loads while the operands stream in behind them.
+  const int Q = 256 / RP;
+  const int r = tid % RP, q = tid / RP;
+  const bool rq = q < Q;
+  const int qc = rq ? q : 0;
+  float v[2][16];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int gg = qc + u * Q;
+      v[t][u] = load_partial<true>(part + ((size_t)(gg < G ? gg : 0) * T + (t < T ? t : 0)) * RP + r);
+    }
+  __builtin_amdgcn_sched_barrier(0);
+
+  const int wave = tid >> 6;
+  const int ct = tid - kWave, nct = 3 * kWave;
+  const int HQ = H >> 2;
+  const int total = T * HQ;
+  float4 xq[KB][4];
+  auto load_batch = [&](int i0) {
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int idx = i0 + k * nct;
+      const int ic = idx < total ? idx : 0;  // past the end: re-read quad 0, never stored
+      const int t = ic / HQ, qq = ic - t * HQ;
+      const float4* xt = reinterpret_cast<const float4*>(x + (size_t)t * S * H) + qq;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (c < S) xq[k][c] = xt[(size_t)c * HQ];
+    }
+  };
+  if (wave >= 1) load_batch(ct);
+  __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    float s = 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (rq && qc + u * Q < G) s += v[t][u];
+    red256[t][tid] = s;
+  }
+  __syncthreads();
+  if (tid < RP)
+    for (int t = 0; t < T; ++t) {
+      float s = 0.f;
+      for (int qi = 0; qi < Q; ++qi) s += red256[t][qi * RP + tid];
+      m_raw[t][tid] = s;
+    }
+  __syncthreads();
+
+  if (wave == 0) {
+    gates_wave<4, false>(&m_raw[0][0], 32, T, S, n, params, iters, eps, true, pre, post, comb,
+                         nullptr);
+    return;
+  }
+
+  // collapse: y[t, i] = sum_c pre[t, c] * x[t, c, i]
+  float pc[2][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      pc[t][c] = (t < T && c < S) ? pre_gate(m_raw[t], c, R, n, eps, params) : 0.f;
+  if (ct < T * S) pre[ct] = pre_gate(m_raw[ct / S], ct % S, R, n, eps, params);
+  for (int i0 = ct; i0 < total; i0 += KB * nct) {
+    if (i0 != ct) load_batch(i0);
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int idx = i0 + k * nct;
+      if (idx < total) {
+        const int t = idx / HQ, qq = idx - t * HQ;
+        reinterpret_cast<float4*>(y + (size_t)t * H)[qq] =
+            collapse4<4>(t == 0 ? pc[0] : pc[1], xq[k], S);
+      }
+    }
+  }
+}
+
+bool decode4_supported(int T, int S, int G) {
+  const int RP = (2 + S) * S + 1;
+  return T >= 1 && T <= 2 && S >= 1 && S <= 4 && G >= 1 && G <= 16 * (256 / RP);
+}
+
+hipError_t launch_decode4_pre(const float* x, const float* fn_w, const float* scale,
+                              const float* base, int T, int S, int H, int iters, float eps,
+                              int G, int chunks_per_range, float* part, unsigned int* counter,
+                              float* pre, float* post, float* comb, float* y, hipStream_t st) {
+  if (!decode4_supported(T, S, G)) return hipErrorInvalidValue;
+  const int R = (2 + S) * S, nrt = (R + 15) / 16;
+  if (nrt == 1)
+    hipLaunchKernelGGL((decode4_pre_kernel<1>), dim3(G), dim3(256), 0, st, x, fn_w, scale, base,
+                       T, S, H, iters, eps, chunks_per_range, part, counter, pre, post, comb, y);
+  else
+    hipLaunchKernelGGL((decode4_pre_kernel<2>), dim3(G), dim3(256), 0, st, x, fn_w, scale, base,
+                       T, S, H, iters, eps, chunks_per_range, part, counter, pre, post, comb, y);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_pre(const float* x, const float* fn_w, const float* scale,

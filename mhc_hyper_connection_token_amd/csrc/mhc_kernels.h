@@ -32,6 +32,14 @@ hipError_t launch_decode_pre(const float* x, const float* fn_w, const float* sca
                              int chunks_per_range, float* part, unsigned int* counter,
                              float* pre, float* post, float* comb, float* y, hipStream_t st);
 
+// Single-launch pre chain for T <= 2 and S <= 4 (same ticket contract), with
+// the collapse operands requested while the partials are being added.
+bool decode4_supported(int T, int S, int G);
+hipError_t launch_decode4_pre(const float* x, const float* fn_w, const float* scale,
+                              const float* base, int T, int S, int H, int iters, float eps,
+                              int G, int chunks_per_range, float* part, unsigned int* counter,
+                              float* pre, float* post, float* comb, float* y, hipStream_t st);
+
 // Post mix.
 hipError_t launch_post(const float* x, const float* f, const float* post, const float* comb,
                        int T, int S, int H, float* x_out, hipStream_t st);

@@ -36,8 +36,9 @@ __global__ __launch_bounds__(256) void partials_kernel(const float* __restrict__
   const int nchunks = (n + 15) >> 4;
   const int c_beg = g * chunks_per_range;
   const int c_end = min(nchunks, c_beg + chunks_per_range);
+  float* pg = part + (size_t)g * T * (R + 1);
   block_partials<NRT, NTT>(x, fn_w, T, n, R, blockIdx.x * (16 * NTT), c_beg, c_end, red,
-                           part + (size_t)g * T * (R + 1));
+                           [=](size_t i, float v) { pg[i] = v; });
 }
 
 template <int NRT, int NTT>

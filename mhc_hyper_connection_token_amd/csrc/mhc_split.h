@@ -9,7 +9,8 @@ namespace mhc {
 // Per-block split-K partials (hyper.rs page, module doc: arithmetic contract,
 // first two lines): for tokens [tok0, tok0 + 16*NTT) and the 16-float K chunks
 // [c_beg, c_end) of the slab, the partial dots with the R weight rows and the
-// partial sum of squares, written to pg[t*(R+1) + r] (r == R: sum of squares).
+// partial sum of squares, handed to sink(t*(R+1) + r, value) (r == R: sum of
+// squares; t is the token's index in the batch).
 // 256 threads = four waves; wave w takes chunks c_beg + w, c_beg + w + 4, ...;
 // the four wave partials are added in wave order through `red`
 // (4 * (NRT*NTT*4 + NTT) * 64 floats of LDS).
@@ -35,11 +36,11 @@ __device__ __forceinline__ float load_partial(const float* p) {
   return *p;
 }
 
-template <int NRT, int NTT, bool COHERENT = false>
+template <int NRT, int NTT, class Sink>
 __device__ __forceinline__ void block_partials(const float* __restrict__ x,
                                                const float* __restrict__ fn_w, int T, int n,
                                                int R, int tok0, int c_beg, int c_end,
-                                               float* red, float* __restrict__ pg) {
+                                               float* red, Sink sink) {
   constexpr int kVals = NRT * NTT * 4 + NTT;  // per lane, per wave
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -152,11 +153,11 @@ __device__ __forceinline__ void block_partials(const float* __restrict__ x,
       const int rt = v / (NTT * 4), tt = (v / 4) % NTT, e = v % 4;
       const int r = rt * 16 + 4 * (l >> 4) + e;
       const int t = tok0 + tt * 16 + (l & 15);
-      if (r < R && t < T) store_partial<COHERENT>(pg + (size_t)t * RP + r, s);
+      if (r < R && t < T) sink((size_t)t * RP + r, s);
     } else {
       const int tt = v - NRT * NTT * 4;
       const int t = tok0 + tt * 16 + (l & 15);
-      if (l < 16 && t < T) store_partial<COHERENT>(pg + (size_t)t * RP + R, s);
+      if (l < 16 && t < T) sink((size_t)t * RP + R, s);
     }
   }
 }
