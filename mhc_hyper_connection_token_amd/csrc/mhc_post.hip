@@ -2,8 +2,8 @@
 //   x_out[t,k,i] = post[t,k] * f[t,i] + sum_j comb[t,j,k] * x[t,j,i]
 //
 // A pure stream: every thread owns one hidden quad (16 bytes) of one token,
-// reads the S source quads and the branch quad once, and writes the S target
-// quads once.  The token's gates are block-uniform (one token per block row),
+// reads the S source quads and the branch quad once (non-temporal: they are
+// not read again by this kernel), and writes the S target quads once.  The token's gates are block-uniform (one token per block row),
 // so they come through scalar loads.  HBM-bound: the bytes per token are
 // 4*(2*S*H + H) plus the gates.
 #include "mhc_device.h"
@@ -32,8 +32,8 @@ __global__ __launch_bounds__(256) void post_kernel(const float* __restrict__ x,
   const float4* xt = reinterpret_cast<const float4*>(x) + (size_t)t * S * HQ + q;
   float4 xv[S];
 #pragma unroll
-  for (int j = 0; j < S; ++j) xv[j] = xt[(size_t)j * HQ];
-  const float4 fv = reinterpret_cast<const float4*>(f)[(size_t)t * HQ + q];
+  for (int j = 0; j < S; ++j) xv[j] = nt_load4(reinterpret_cast<const float*>(xt + (size_t)j * HQ));
+  const float4 fv = nt_load4(f + ((size_t)t * HQ + q) * 4);
   float4* ot = reinterpret_cast<float4*>(out) + (size_t)t * S * HQ + q;
 #pragma unroll
   for (int k = 0; k < S; ++k) {
