@@ -62,10 +62,10 @@ def alloc_out(T, S, H, torch):
     return (e(T, S), e(T, S), e(T, S, S), e(T, H)), e(T, S, H)
 
 
-def run_kernels_only(n, mhc, torch, CONFIGS, make_site):
+def run_kernels_only(n, mhc, torch, CONFIGS, make_site, workloads=("prefill", "decode")):
     """A handful of launches of each workload kernel plus a plain 256 MiB device
     copy (the reference for scaling rocprof's byte counters)."""
-    for name in ("prefill", "decode"):
+    for name in workloads:
         c = CONFIGS[name]
         t = to_dev(make_site(c), torch)
         (pre_o, xo) = alloc_out(c.T, c.S, c.H, torch)
@@ -263,6 +263,8 @@ def main():
     ap.add_argument("--decode-sites", type=int, default=2000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels-only", type=int, default=0)
+    ap.add_argument("--workloads", default="prefill,decode",
+                    help="configs (mhc_inputs.CONFIGS names) run by --kernels-only")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="write the measured traffic file from two rocprofv3 counter runs")
     args = ap.parse_args()
@@ -286,7 +288,8 @@ def main():
         sys.exit(1)
     mhc.load_library()
     if args.kernels_only:
-        run_kernels_only(args.kernels_only, mhc, torch, CONFIGS, make_site)
+        run_kernels_only(args.kernels_only, mhc, torch, CONFIGS, make_site,
+                         tuple(w for w in args.workloads.split(",") if w))
         return
 
     # ---- prefill chunk: the timed workload
