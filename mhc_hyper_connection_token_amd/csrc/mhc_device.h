@@ -68,10 +68,29 @@ __device__ __forceinline__ float sum_row16(float v) {
 // ---------------------------------------------------------------- Sinkhorn
 // Two lane layouts for the S x S block (entries outside S x S hold 0 and stay 0,
 // so padded sums equal the true sums):
-//   L = 4 (S <= 4): lane = 16*j + 4*u + k, four tokens u per wavefront;
-//                   row sums over k = lane bits 0-1, column sums over j = bits 4-5.
+//   L = 4 (S <= 4): four tokens u per wavefront, u = lane bits 4-5; row j =
+//                   lane bits 2-3; column k = lane bits 0-1 for even j and
+//                   3 - (bits 0-1) for odd j.  A row is one quad (sums by quad
+//                   permutes); the four entries of a column sit at lanes
+//                   {k, 7-k, 8+k, 15-k} of the token's 16-lane row, paired by
+//                   the half-row mirror and then by rotation by 8, so both
+//                   passes are two DPP adds.
 //   L = 8 (S <= 8): lane = 8*j + k, one token per wavefront;
 //                   row sums over bits 0-2, column sums over bits 3-5.
+// Every reduction is a butterfly: all lanes of a row (column) end with the
+// same bits.
+template <int L>
+__device__ __forceinline__ void sinkhorn_lane_entry(int lane, int& u, int& j, int& k) {
+  if (L == 4) {
+    u = lane >> 4;
+    j = (lane >> 2) & 3;
+    k = (j & 1) ? 3 - (lane & 3) : (lane & 3);
+  } else {
+    u = 0;
+    j = lane >> 3;
+    k = lane & 7;
+  }
+}
 template <int L>
 __device__ __forceinline__ float row_sum(float v) {
   v = sum_xor1_2(v);
@@ -80,7 +99,11 @@ __device__ __forceinline__ float row_sum(float v) {
 }
 template <int L>
 __device__ __forceinline__ float col_sum(float v) {
-  if (L == 8) v = sum_xor8_in16(v);
+  if (L == 4) {
+    v += dpp<0x141>(v);  // row_half_mirror: lane k <-> 7-k (rows 0 and 1, 2 and 3)
+    return v + dpp<0x128>(v);  // row_ror:8: rows 0+1 <-> 2+3
+  }
+  v = sum_xor8_in16(v);
   v = swap16_sum(v);
   return swap32_sum(v);
 }
@@ -186,15 +209,7 @@ __device__ __forceinline__ void gates_wave(const float* mraw, int ldm, int ntok,
   }
   // comb
   int j, k, u;
-  if (L == 4) {
-    j = lane >> 4;
-    u = (lane >> 2) & 3;
-    k = lane & 3;
-  } else {
-    j = lane >> 3;
-    u = 0;
-    k = lane & 7;
-  }
+  sinkhorn_lane_entry<L>(lane, u, j, k);
   const bool valid = (j < S) && (k < S) && (u < ntok);
   float c = 0.0f;
   if (valid) {
