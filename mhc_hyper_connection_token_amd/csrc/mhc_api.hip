@@ -205,8 +205,10 @@ int mhc_site_pre(const float* x, const float* fn_w, const float* scale, const fl
                                                 p.cpr, part, sc.counter, pre, post, comb, y, st);
     return e == hipSuccess ? MHC_OK : MHC_EHIP;
   }
-  if (mhc::launch_partials(x, fn_w, T, n, R, p.ntt, p.G, p.cpr, part, st) != hipSuccess)
-    return MHC_EHIP;
+  const hipError_t pe = (T <= 16 && S <= 4)
+                           ? mhc::launch_small_partials(x, fn_w, T, S, H, p.G, p.cpr, part, st)
+                           : mhc::launch_partials(x, fn_w, T, n, R, p.ntt, p.G, p.cpr, part, st);
+  if (pe != hipSuccess) return MHC_EHIP;
   if (mhc::launch_finish(x, part, p.G, T, S, H, scale, base, iters, eps, pre, post, comb, y,
                          st) != hipSuccess)
     return MHC_EHIP;

@@ -9,7 +9,8 @@
 // the kernel cannot stall on scheduling.  Results are bit-identical to the
 // two-kernel path for the same G.
 //
-// S <= 4 (decode4_pre_kernel): partials, then a ticket counter; the block
+// S <= 4 (decode4_pre_kernel): partials on the vector ALU (the same routine as
+// the small-batch partials kernel), then a ticket counter; the block
 // that draws the last ticket requests every partial and, right behind them,
 // the collapse operands, adds the partials, and then splits: wave 0 runs the
 // gates and the Sinkhorn while the other waves compute the pre gates
@@ -122,16 +123,14 @@ __global__ __launch_bounds__(256) void decode_pre_kernel(
   }
 }
 
-template <int NRT>
+template <int RPT>
 __global__ __launch_bounds__(256) void decode4_pre_kernel(
     const float* __restrict__ x, const float* __restrict__ fn_w, const float* __restrict__ scale,
     const float* __restrict__ base, int T, int S, int H, int iters, float eps,
     int chunks_per_range, float* __restrict__ part, unsigned int* __restrict__ counter,
     float* __restrict__ pre, float* __restrict__ post, float* __restrict__ comb,
     float* __restrict__ y) {
-  constexpr int kVals = NRT * 4 + 1;
   constexpr int KB = 6;  // collapse quads in flight per collapse thread
-  __shared__ float red[4 * kVals * kWave];
   __shared__ float red256[2][256];
   __shared__ float m_raw[2][32];
   __shared__ float params[3 + 24];
@@ -147,7 +146,7 @@ __global__ __launch_bounds__(256) void decode4_pre_kernel(
   stage_site_params(scale, base, R, params);
 
   float* pg = part + (size_t)g * T * RP;
-  block_partials<NRT, 1>(x, fn_w, T, n, R, 0, c_beg, c_end, red,
+  small_partials<2, RPT>(x, fn_w, T, n, R, c_beg * 16, min(n, c_end * 16),
                          [=](size_t i, float v) { store_partial<true>(pg + i, v); });
   __builtin_amdgcn_s_waitcnt(0);  // this thread's stores are complete ...
   __syncthreads();                // ... and so are those of the whole block
@@ -251,14 +250,17 @@ hipError_t launch_decode4_pre(const float* x, const float* fn_w, const float* sc
                               int G, int chunks_per_range, float* part, unsigned int* counter,
                               float* pre, float* post, float* comb, float* y, hipStream_t st) {
   if (!decode4_supported(T, S, G)) return hipErrorInvalidValue;
-  const int R = (2 + S) * S, nrt = (R + 15) / 16;
-  if (nrt == 1)
-    hipLaunchKernelGGL((decode4_pre_kernel<1>), dim3(G), dim3(256), 0, st, x, fn_w, scale, base,
-                       T, S, H, iters, eps, chunks_per_range, part, counter, pre, post, comb, y);
-  else
-    hipLaunchKernelGGL((decode4_pre_kernel<2>), dim3(G), dim3(256), 0, st, x, fn_w, scale, base,
-                       T, S, H, iters, eps, chunks_per_range, part, counter, pre, post, comb, y);
-  return hipGetLastError();
+  const int rpt = small_rows_per_thread(S);
+#define MHC_D4(RP_)                                                                           \
+  if (rpt == RP_) {                                                                            \
+    hipLaunchKernelGGL((decode4_pre_kernel<RP_>), dim3(G), dim3(256), 0, st, x, fn_w, scale,   \
+                       base, T, S, H, iters, eps, chunks_per_range, part, counter, pre, post,   \
+                       comb, y);                                                               \
+    return hipGetLastError();                                                                  \
+  }
+  MHC_D4(1) MHC_D4(2) MHC_D4(4)
+#undef MHC_D4
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_pre(const float* x, const float* fn_w, const float* scale,

@@ -9,6 +9,12 @@ namespace mhc {
 hipError_t launch_partials(const float* x, const float* fn_w, int T, int n, int R, int ntt,
                            int G, int chunks_per_range, float* part, hipStream_t st);
 
+// Vector-ALU split-K partials for a small batch (T <= 16, S <= 4), per token in
+// the order the single-launch decode kernel uses; same part layout.
+int small_rows_per_thread(int S);
+hipError_t launch_small_partials(const float* x, const float* fn_w, int T, int S, int H, int G,
+                                 int chunks_per_range, float* part, hipStream_t st);
+
 // Reduce partials, gates, Sinkhorn, collapse.
 hipError_t launch_finish(const float* x, const float* part, int G, int T, int S, int H,
                          const float* scale, const float* base, int iters, float eps,

@@ -50,6 +50,52 @@ static hipError_t launch_partials_t(const float* x, const float* fn_w, int T, in
   return hipGetLastError();
 }
 
+// Small batches (T <= 16, S <= 4): the vector-ALU partials, one token at a time
+// in the same order as the single-launch decode kernel, so a token's result
+// does not depend on the batch it is in.
+template <int RPT>
+__global__ __launch_bounds__(256) void small_partials_kernel(const float* __restrict__ x,
+                                                             const float* __restrict__ fn_w,
+                                                             int T, int n, int R,
+                                                             int chunks_per_range,
+                                                             float* __restrict__ part) {
+  const int g = blockIdx.x;
+  const int k_beg = g * chunks_per_range * 16;
+  const int k_end = min(n, k_beg + chunks_per_range * 16);
+  float* pg = part + (size_t)g * T * (R + 1);
+  small_partials<16, RPT>(x, fn_w, T, n, R, k_beg, k_end,
+                          [=](size_t i, float v) { pg[i] = v; });
+}
+
+int small_rows_per_thread(int S) {
+  const int rows = (2 + S) * S + 1;  // R rows and the sum of squares
+  const int rpt = (rows + 7) / 8;
+  return rpt <= 1 ? 1 : (rpt <= 2 ? 2 : (rpt <= 4 ? 4 : 0));
+}
+
+hipError_t launch_small_partials(const float* x, const float* fn_w, int T, int S, int H, int G,
+                                 int chunks_per_range, float* part, hipStream_t st) {
+  if (T < 1 || T > 16) return hipErrorInvalidValue;
+  const int n = S * H, R = (2 + S) * S;
+  switch (small_rows_per_thread(S)) {
+    case 1:
+      hipLaunchKernelGGL((small_partials_kernel<1>), dim3(G), dim3(256), 0, st, x, fn_w, T, n, R,
+                         chunks_per_range, part);
+      break;
+    case 2:
+      hipLaunchKernelGGL((small_partials_kernel<2>), dim3(G), dim3(256), 0, st, x, fn_w, T, n, R,
+                         chunks_per_range, part);
+      break;
+    case 4:
+      hipLaunchKernelGGL((small_partials_kernel<4>), dim3(G), dim3(256), 0, st, x, fn_w, T, n, R,
+                         chunks_per_range, part);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_partials(const float* x, const float* fn_w, int T, int n, int R, int ntt,
                            int G, int chunks_per_range, float* part, hipStream_t st) {
   const int nrt = (R + 15) / 16;

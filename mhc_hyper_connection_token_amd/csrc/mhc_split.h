@@ -110,15 +110,29 @@ __device__ __forceinline__ void block_partials(const float* __restrict__ x,
       ss[tt] = fmaf(b[tt].z, b[tt].z, ss[tt]);
       ss[tt] = fmaf(b[tt].w, b[tt].w, ss[tt]);
     }
+    // Component-major issue: consecutive MFMAs go to different accumulators, so
+    // none waits for the previous one (each accumulator still adds x, y, z, w
+    // in that order).
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) {
+      for (int tt = 0; tt < NTT; ++tt)
         acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rt].x, b[tt].x, acc[rt][tt], 0, 0, 0);
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt)
         acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rt].y, b[tt].y, acc[rt][tt], 0, 0, 0);
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt)
         acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rt].z, b[tt].z, acc[rt][tt], 0, 0, 0);
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt)
         acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rt].w, b[tt].w, acc[rt][tt], 0, 0, 0);
-      }
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) a0[rt] = a1[rt];
 #pragma unroll
@@ -158,6 +172,72 @@ __device__ __forceinline__ void block_partials(const float* __restrict__ x,
       const int tt = v - NRT * NTT * 4;
       const int t = tok0 + tt * 16 + (l & 15);
       if (l < 16 && t < T) sink((size_t)t * RP + R, s);
+    }
+  }
+}
+
+// Split-K partials of a small batch (T <= TMAX tokens) on the vector ALU: for
+// every token t and row r < R the dot of fn_w[r, k_beg:k_end] with
+// x[t, k_beg:k_end], and at r == R the sum of squares of that slice, handed to
+// sink(t*(R+1) + r, value).  256 threads = 8 row slots x 32 lanes: lane l of
+// slot s takes the column quads l, l + 32, ... and rows s, s + 8, s + 16, ...
+// (RPT of them), so every weight load is a coalesced run of one row.  A
+// token's arithmetic (the order of its products and of the 32-lane butterfly
+// sum) does not depend on T or TMAX: a token's partials are the same in any
+// small batch.  k_beg and k_end are multiples of 4.
+template <int TMAX, int RPT, class Sink>
+__device__ __forceinline__ void small_partials(const float* __restrict__ x,
+                                               const float* __restrict__ fn_w, int T, int n,
+                                               int R, int k_beg, int k_end, Sink sink) {
+  const int tid = threadIdx.x;
+  const int l = tid & 31, slot = tid >> 5;
+  const int nq = (k_end - k_beg) >> 2;
+  float acc[RPT][TMAX];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) acc[i][t] = 0.f;
+  for (int q = l; q < nq; q += 32) {
+    const int col = k_beg + 4 * q;
+    // all loads of this column quad first (branch-free: clamped rows / tokens)
+    float4 w[RPT], xv[TMAX];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = slot + 8 * i;
+      w[i] = *reinterpret_cast<const float4*>(fn_w + (size_t)(r < R ? r : 0) * n + col);
+    }
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t)
+      xv[t] = *reinterpret_cast<const float4*>(x + (size_t)(t < T ? t : 0) * n + col);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = slot + 8 * i;
+      const float4 wi = r == R ? make_float4(1.f, 1.f, 1.f, 1.f) : w[i];
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t) {
+        // the sum-of-squares row multiplies x by itself
+        const float4 a = r == R ? xv[t] : wi;
+        float v = acc[i][t];
+        v = fmaf(a.x, xv[t].x, v);
+        v = fmaf(a.y, xv[t].y, v);
+        v = fmaf(a.z, xv[t].z, v);
+        v = fmaf(a.w, xv[t].w, v);
+        acc[i][t] = v;
+      }
+    }
+  }
+  const int RP = R + 1;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = slot + 8 * i;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      float v = acc[i][t];
+      v = sum_xor1_2(v);
+      v = sum_xor4_in8(v);
+      v = sum_xor8_in16(v);
+      v = swap16_sum(v);
+      if (l == 0 && t < T && r <= R) sink((size_t)t * RP + r, v);
     }
   }
 }
