@@ -58,6 +58,12 @@ def _load():
         lib.mhc_oracle_sinkhorn.argtypes = [dp, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_double, dp]
         lib.mhc_oracle_sinkhorn.restype = ctypes.c_int
+        lib.mhc_oracle_rmsnorm.argtypes = [fp, fp, ctypes.c_long, ctypes.c_int,
+                                           ctypes.c_double, dp]
+        lib.mhc_oracle_rmsnorm.restype = ctypes.c_int
+        lib.mhc_oracle_q8.argtypes = [fp, ctypes.c_long, ctypes.c_int,
+                                      ctypes.POINTER(ctypes.c_int8), fp]
+        lib.mhc_oracle_q8.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -142,3 +148,29 @@ def sinkhorn(z, iters: int, eps: float):
     if rc != 0:
         raise ValueError(f"mhc_oracle_sinkhorn rejected its arguments (rc={rc})")
     return out
+
+
+def rmsnorm(y, nw, norm_eps):
+    """O8: z = y * nw / sqrt(mean(y^2) + norm_eps) per token, in double precision.
+    y [T, H] float32, nw [H] float32 -> z [T, H] float64."""
+    lib = _load()
+    y, py = _f32(y)
+    nw, pn = _f32(nw)
+    T, H = y.shape
+    z, pz = _f64(np.empty((T, H)))
+    if lib.mhc_oracle_rmsnorm(py, pn, T, H, float(norm_eps), pz) != 0:
+        raise ValueError("mhc_oracle_rmsnorm rejected its arguments")
+    return z
+
+
+def q8(z):
+    """O9: the int8 codes and fp32 block scales of z [T, H] (float32, H % 32 == 0),
+    decided in fp32.  Returns (q [T, H] int8, d [T, H/32] float32)."""
+    lib = _load()
+    z, pz = _f32(z)
+    T, H = z.shape
+    q = np.empty((T, H), dtype=np.int8)
+    d, pd = _f32(np.empty((T, H // 32), dtype=np.float32))
+    if lib.mhc_oracle_q8(pz, T, H, q.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)), pd) != 0:
+        raise ValueError("mhc_oracle_q8 rejected its arguments")
+    return q, d

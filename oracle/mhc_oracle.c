@@ -241,6 +241,60 @@ int mhc_oracle_post(const float *x, const float *f, const float *post,
   return fan_out(&jb, T, nthreads);
 }
 
+/* ------------------------------------------------------------------------ */
+/* Branch-input epilogue (hc_fused_gate.rs page, the v4z timing block: the
+ * served rms-norm-and-q8 launch that the fused v4z kernel folds into the pre
+ * chain, with a norm weight nw and epsilon 1e-5, writing z, an int8 code
+ * vector q[H] and fp32 scales d[H/32]).  The page names the buffers but not the
+ * formulas; the readings taken are:
+ *   O8  z[i] = y[i] * nw[i] / sqrt(mean_i(y^2) + norm_eps)      (RMS norm of y)
+ *   O9  per block of 32 consecutive entries of z (a q8 block):
+ *         amax = max |z|;  d = amax / 127;  id = 1/d (0 when d == 0);
+ *         q[i] = z[i] * id rounded to nearest, ties away from zero.
+ * O8 is computed in double precision.  O9 turns floats into integers, so it is
+ * evaluated in the precision the kernel uses: fp32, on the fp32 z given. */
+
+/* O8 for T tokens: y [T][H] (fp32), nw [H] -> z [T][H] (double). */
+int mhc_oracle_rmsnorm(const float *y, const float *nw, long T, int H,
+                       double norm_eps, double *z) {
+  if (T < 0 || H < 1 || !(norm_eps > 0.0)) return 1;
+  if (T == 0) return 0;
+  if (!y || !nw || !z) return 1;
+  for (long t = 0; t < T; ++t) {
+    const float *yt = y + t * H;
+    double ss = 0.0;
+    for (int i = 0; i < H; ++i) ss += (double)yt[i] * (double)yt[i];
+    const double r = 1.0 / sqrt(ss / (double)H + norm_eps);
+    for (int i = 0; i < H; ++i) z[t * H + i] = (double)yt[i] * r * (double)nw[i];
+  }
+  return 0;
+}
+
+/* O9 for T tokens: z [T][H] (fp32, H a multiple of 32) -> q [T][H], d [T][H/32]. */
+int mhc_oracle_q8(const float *z, long T, int H, signed char *q, float *d) {
+  if (T < 0 || H < 32 || H % 32 != 0) return 1;
+  if (T == 0) return 0;
+  if (!z || !q || !d) return 1;
+  for (long t = 0; t < T; ++t) {
+    for (int b = 0; b < H / 32; ++b) {
+      const float *zb = z + t * H + b * 32;
+      float amax = 0.0f;
+      for (int i = 0; i < 32; ++i) {
+        const float a = fabsf(zb[i]);
+        if (a > amax) amax = a;
+      }
+      const float db = amax / 127.0f;
+      const float id = db != 0.0f ? 1.0f / db : 0.0f;
+      d[t * (H / 32) + b] = db;
+      for (int i = 0; i < 32; ++i) {
+        const float v = zb[i] * id;
+        q[t * H + b * 32 + i] = (signed char)roundf(v);
+      }
+    }
+  }
+  return 0;
+}
+
 /* Sinkhorn alone, on S x S logits z (row-major), for the structural checks:
  * comb = Sinkhorn(exp(z)). */
 int mhc_oracle_sinkhorn(const double *z, int S, int iters, double eps,

@@ -60,6 +60,17 @@ MUTANTS = {
         "acc += (double)comb[k * S + j] * (double)xt[(long)j * H + i];"),
     "post mix drops the branch term": lambda s: s.replace(
         "double acc = (double)post[k] * (double)ft[i];", "double acc = 0.0;"),
+    "norm mean over H + 1": lambda s: s.replace(
+        "sqrt(ss / (double)H + norm_eps)", "sqrt(ss / (double)(H + 1) + norm_eps)"),
+    "norm eps dropped": lambda s: s.replace(
+        "sqrt(ss / (double)H + norm_eps)", "sqrt(ss / (double)H)"),
+    "norm weight ignored": lambda s: s.replace(
+        "z[t * H + i] = (double)yt[i] * r * (double)nw[i];", "z[t * H + i] = (double)yt[i] * r;"),
+    "q8 scale over 128": lambda s: s.replace("amax / 127.0f", "amax / 128.0f"),
+    "q8 ties to even": lambda s: s.replace("(signed char)roundf(v)", "(signed char)rintf(v)"),
+    "q8 truncates": lambda s: s.replace("(signed char)roundf(v)", "(signed char)v"),
+    "q8 blocks of 16": lambda s: s.replace("const float *zb = z + t * H + b * 32;",
+                                           "const float *zb = z + t * H + b * 16;"),
 }
 
 

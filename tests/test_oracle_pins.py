@@ -412,3 +412,82 @@ def test_oracle_rejects_what_the_pages_refuse():
         oracle.site_pre(d["x"], d["fn_w"], d["scale"], d["base"], 3, 0.0)
     with pytest.raises(ValueError):
         oracle.sinkhorn(np.zeros((2, 2)), 0, 1e-6)
+
+
+# ------------------------------------------------------------------ branch-input epilogue
+# O8 (RMS norm of y with weight nw) and O9 (q8 codes), hc_fused_gate.rs page, v4z
+# timing block.  The page fixes the buffers (z, int8 q[H], fp32 d[H/32]) and the
+# norm epsilon 1e-5, not the formulas; the pins below fix what the readings mean.
+NORM_EPS = 1e-5
+
+
+@pytest.mark.parametrize("a", [0.25, 3.0])
+def test_rmsnorm_constant_row_closed_form(a):
+    H = 64
+    y = np.full((1, H), a, dtype=np.float32)
+    nw = np.linspace(0.5, 1.5, H).astype(np.float32)
+    z = oracle.rmsnorm(y, nw, NORM_EPS)
+    want = np.float64(a) / np.sqrt(np.float64(a) ** 2 + NORM_EPS) * nw.astype(np.float64)
+    np.testing.assert_allclose(z[0], want, rtol=1e-14, atol=0)
+
+
+def test_rmsnorm_output_has_unit_weighted_rms_and_scale_invariance():
+    rng = np.random.default_rng(11)
+    y = rng.standard_normal((3, 256)).astype(np.float32)
+    nw = rng.uniform(0.5, 2.0, 256).astype(np.float32)
+    z = oracle.rmsnorm(y, nw, NORM_EPS)
+    ms = (y.astype(np.float64) ** 2).mean(axis=1)
+    # mean((z / nw)^2) = ms / (ms + eps)
+    np.testing.assert_allclose(((z / nw) ** 2).mean(axis=1), ms / (ms + NORM_EPS), rtol=1e-12)
+    c = 2.0 ** 8
+    z2 = oracle.rmsnorm(y * np.float32(c), nw, NORM_EPS)
+    # scaling y by c changes z only through eps: z2 / z = sqrt(ms + eps) / sqrt(ms + eps / c^2)
+    ratio = np.sqrt(ms + NORM_EPS) / np.sqrt(ms + NORM_EPS / c ** 2)
+    np.testing.assert_allclose(z2, z * ratio[:, None], rtol=1e-12)
+    # the mean is over the row (hidden), one scale per token
+    assert not np.allclose(z[0] / z[0].max(), z[1] / z[1].max())
+
+
+def test_rmsnorm_matches_high_precision_brute_force():
+    rng = np.random.default_rng(5)
+    y = rng.standard_normal((2, 40)).astype(np.float32)
+    nw = rng.uniform(0.5, 1.5, 40).astype(np.float32)
+    z = oracle.rmsnorm(y, nw, NORM_EPS)
+    getcontext().prec = 40
+    for t in range(2):
+        ys = [Decimal(float(v)) for v in y[t]]
+        ss = sum((v * v for v in ys), Decimal(0))
+        r = 1 / (ss / len(ys) + Decimal(NORM_EPS)).sqrt()
+        want = [float(v * r * Decimal(float(w))) for v, w in zip(ys, nw)]
+        np.testing.assert_allclose(z[t], want, rtol=1e-14)
+
+
+def test_q8_scale_is_block_max_over_127_and_the_max_maps_to_127():
+    rng = np.random.default_rng(3)
+    z = rng.standard_normal((2, 96)).astype(np.float32)
+    q, d = oracle.q8(z)
+    for t in range(2):
+        for b in range(3):
+            blk = z[t, 32 * b:32 * b + 32]
+            amax = np.max(np.abs(blk))
+            assert d[t, b] == np.float32(amax) / np.float32(127.0)
+            i = int(np.argmax(np.abs(blk)))
+            assert q[t, 32 * b + i] == (127 if blk[i] > 0 else -127)
+    assert np.all(np.abs(q.astype(np.int32)) <= 127)
+    # reconstruction within half a step
+    rec = q.astype(np.float64) * np.repeat(d.astype(np.float64), 32, axis=1)
+    step = np.repeat(d.astype(np.float64), 32, axis=1)
+    assert np.all(np.abs(rec - z) <= 0.5 * step * (1 + 1e-6) + 1e-12)
+
+
+def test_q8_ties_round_away_from_zero_and_zero_blocks():
+    z = np.zeros((1, 64), dtype=np.float32)
+    z[0, 0] = 127.0             # amax 127 -> d = 1, id = 1: codes equal the values
+    z[0, 1] = 2.5
+    z[0, 2] = -2.5
+    z[0, 3] = 0.5
+    z[0, 4] = -0.49
+    q, d = oracle.q8(z)
+    assert d[0, 0] == 1.0 and d[0, 1] == 0.0
+    assert list(q[0, :5]) == [127, 3, -3, 1, 0]
+    assert np.all(q[0, 32:] == 0)   # an all-zero block: d = 0 and all codes 0
