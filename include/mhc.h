@@ -107,6 +107,31 @@ int mhc_site_post(const float* x, const float* f, const float* post, const float
                   int T, int streams, int hidden, float* x_out, void* stream);
 
 /*
+ * mhc_site_pre_zq8 -- mhc_site_pre followed by the branch-input epilogue: the
+ * RMS norm of y with weight nw and its int8 q8 encoding (the norm-and-q8 step
+ * that the fused "v4z" pre kernel of the hc_fused_gate.rs page folds into the
+ * pre chain; epsilon 1e-5 there).  Per token t, after y[t,:] as above:
+ *   z[t,i] = y[t,i] * nw[i] / sqrt(mean_i(y[t,i]^2) + norm_eps)
+ *   per block of 32 consecutive i:  d[t,b] = max|z| / 127,
+ *   q[t,i] = z[t,i] * (1/d[t,b]) rounded to nearest, ties away from zero
+ *   (an all-zero block gives d = 0 and q = 0).  d and 1/d are IEEE fp32
+ *   divisions, so q and d are a function of the fp32 z written.
+ *
+ * Arguments: as mhc_site_pre, plus
+ *   nw        [H]         norm weight (read only)
+ *   norm_eps              > 0 and finite
+ *   z         [T][H]      out (fp32)
+ *   q         [T][H]      out (int8)
+ *   d         [T][H/32]   out (fp32)
+ * hidden must be a multiple of 32 and at most 8192 (MHC_EALIGN / MHC_EUNSUPPORTED).
+ * Outputs must not overlap any input or each other (MHC_EOVERLAP).
+ */
+int mhc_site_pre_zq8(const float* x, const float* fn_w, const float* scale, const float* base,
+                     const float* nw, int T, int streams, int hidden, int iters, float eps,
+                     float norm_eps, float* pre, float* post, float* comb, float* y, float* z,
+                     signed char* q, float* d, void* stream);
+
+/*
  * Argument checks alone: return exactly the code mhc_site_pre / mhc_site_post
  * would return for these arguments before enqueuing any work (MHC_OK if the
  * call would go ahead).  They make no HIP call and are safe without a GPU.
@@ -116,6 +141,11 @@ int mhc_site_pre_check(const float* x, const float* fn_w, const float* scale, co
                        const float* pre, const float* post, const float* comb, const float* y);
 int mhc_site_post_check(const float* x, const float* f, const float* post, const float* comb,
                         int T, int streams, int hidden, const float* x_out);
+int mhc_site_pre_zq8_check(const float* x, const float* fn_w, const float* scale,
+                           const float* base, const float* nw, int T, int streams, int hidden,
+                           int iters, float eps, float norm_eps, const float* pre,
+                           const float* post, const float* comb, const float* y, const float* z,
+                           const signed char* q, const float* d);
 
 /* Static text for a return code (never NULL). */
 const char* mhc_status_string(int status);

@@ -17,14 +17,15 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["site_pre", "site_post", "site_pre_check", "site_post_check", "load_library",
-           "MhcError", "LIB_PATH", "EXPORTED_SYMBOLS", "STATUS"]
+__all__ = ["site_pre", "site_post", "site_pre_zq8", "site_pre_check", "site_post_check",
+           "site_pre_zq8_check", "load_library", "MhcError", "LIB_PATH", "EXPORTED_SYMBOLS",
+           "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmhc.so")
 
-EXPORTED_SYMBOLS = ("mhc_site_pre", "mhc_site_post", "mhc_site_pre_check",
-                    "mhc_site_post_check", "mhc_status_string")
+EXPORTED_SYMBOLS = ("mhc_site_pre", "mhc_site_post", "mhc_site_pre_zq8", "mhc_site_pre_check",
+                    "mhc_site_post_check", "mhc_site_pre_zq8_check", "mhc_status_string")
 
 STATUS = {0: "MHC_OK", 1: "MHC_EINVAL", 2: "MHC_EALIGN", 3: "MHC_EUNSUPPORTED",
           4: "MHC_EHIP", 5: "MHC_EOVERLAP"}
@@ -56,6 +57,12 @@ def load_library() -> ctypes.CDLL:
     lib.mhc_site_pre_check.restype = i
     lib.mhc_site_post_check.argtypes = [vp, vp, vp, vp, i, i, i, vp]
     lib.mhc_site_post_check.restype = i
+    lib.mhc_site_pre_zq8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, fl, fl, vp, vp, vp, vp,
+                                     vp, vp, vp, vp]
+    lib.mhc_site_pre_zq8.restype = i
+    lib.mhc_site_pre_zq8_check.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, fl, fl, vp, vp, vp,
+                                           vp, vp, vp, vp]
+    lib.mhc_site_pre_zq8_check.restype = i
     lib.mhc_status_string.argtypes = [i]
     lib.mhc_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -112,6 +119,38 @@ def site_pre(x, fn_w, scale, base, iters: int, eps: float, *, out=None, stream=N
     return out
 
 
+def site_pre_zq8(x, fn_w, scale, base, nw, iters: int, eps: float, norm_eps: float = 1e-5, *,
+                 out=None, stream=None):
+    """Pre half of a site plus the branch-input epilogue (RMS norm of y with weight nw,
+    then q8 codes).  Returns (pre, post, comb, y, z [T,H] f32, q [T,H] int8, d [T,H/32] f32);
+    `out` may supply that tuple."""
+    import torch
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be [T, S, H]")
+    T, S, H = x.shape
+    R = (2 + S) * S
+    px = _dev(x, "x")
+    pw = _dev(fn_w, "fn_w", (R, S * H))
+    ps = _dev(scale, "scale", (3,))
+    pb = _dev(base, "base", (R,))
+    pn = _dev(nw, "nw", (H,))
+    if out is None:
+        e = lambda s, dt=torch.float32: torch.empty(s, device=x.device, dtype=dt)  # noqa: E731
+        out = (e((T, S)), e((T, S)), e((T, S, S)), e((T, H)), e((T, H)), e((T, H), torch.int8),
+               e((T, H // 32)))
+    pre, post, comb, y, z, q, d = out
+    if q.dtype != torch.int8 or not q.is_cuda or not q.is_contiguous() or tuple(q.shape) != (T, H):
+        raise ValueError("q must be a contiguous int8 GPU tensor of shape [T, H]")
+    ptrs = (_dev(pre, "pre", (T, S)), _dev(post, "post", (T, S)), _dev(comb, "comb", (T, S, S)),
+            _dev(y, "y", (T, H)), _dev(z, "z", (T, H)), q.data_ptr(), _dev(d, "d", (T, H // 32)))
+    rc = lib.mhc_site_pre_zq8(px, pw, ps, pb, pn, T, S, H, int(iters), float(eps),
+                              float(norm_eps), *ptrs, _stream_handle(stream))
+    if rc != 0:
+        raise MhcError("mhc_site_pre_zq8", rc, _status_text(lib, rc))
+    return out
+
+
 def site_post(x, f, post, comb, *, out=None, stream=None):
     """Post half of a site: x' [T,S,H] from x [T,S,H], f [T,H], post [T,S], comb [T,S,S]."""
     import torch
@@ -143,3 +182,11 @@ def site_pre_check(x_ptr, fn_w_ptr, scale_ptr, base_ptr, T, S, H, iters, eps,
 def site_post_check(x_ptr, f_ptr, post_ptr, comb_ptr, T, S, H, out_ptr) -> int:
     lib = load_library()
     return lib.mhc_site_post_check(x_ptr, f_ptr, post_ptr, comb_ptr, T, S, H, out_ptr)
+
+
+def site_pre_zq8_check(x_ptr, fn_w_ptr, scale_ptr, base_ptr, nw_ptr, T, S, H, iters, eps,
+                       norm_eps, pre_ptr, post_ptr, comb_ptr, y_ptr, z_ptr, q_ptr, d_ptr) -> int:
+    lib = load_library()
+    return lib.mhc_site_pre_zq8_check(x_ptr, fn_w_ptr, scale_ptr, base_ptr, nw_ptr, T, S, H,
+                                      iters, float(eps), float(norm_eps), pre_ptr, post_ptr,
+                                      comb_ptr, y_ptr, z_ptr, q_ptr, d_ptr)

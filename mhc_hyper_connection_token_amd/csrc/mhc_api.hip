@@ -215,6 +215,58 @@ int mhc_site_pre(const float* x, const float* fn_w, const float* scale, const fl
   return MHC_OK;
 }
 
+int mhc_site_pre_zq8_check(const float* x, const float* fn_w, const float* scale,
+                           const float* base, const float* nw, int T, int streams, int hidden,
+                           int iters, float eps, float norm_eps, const float* pre,
+                           const float* post, const float* comb, const float* y, const float* z,
+                           const signed char* q, const float* d) {
+  // size checks first (as in mhc_site_pre_check), then pointers
+  int rc = check_shape(T, streams, hidden);
+  if (rc) return rc;
+  if (iters < 1 || !(eps > 0.0f) || !std::isfinite(eps)) return MHC_EINVAL;
+  if (!(norm_eps > 0.0f) || !std::isfinite(norm_eps)) return MHC_EINVAL;
+  if (hidden % 32 != 0) return MHC_EALIGN;
+  if (!mhc::zq8_supported(hidden)) return MHC_EUNSUPPORTED;
+  if ((rc = mhc_site_pre_check(x, fn_w, scale, base, T, streams, hidden, iters, eps, pre, post,
+                               comb, y)))
+    return rc;
+  if (T == 0) return MHC_OK;
+  const void* ptrs[] = {nw, z, q, d};
+  for (const void* p : ptrs)
+    if (!p) return MHC_EINVAL;
+  for (const void* p : ptrs)
+    if ((rc = check_ptr(p))) return rc;
+  const size_t S = streams, H = hidden, Tz = T, R = (2 + S) * S;
+  const Span in[] = {span(x, Tz * S * H * 4), span(fn_w, R * S * H * 4), span(scale, 12),
+                     span(base, R * 4), span(nw, H * 4)};
+  const Span out[] = {span(pre, Tz * S * 4), span(post, Tz * S * 4), span(comb, Tz * S * S * 4),
+                      span(y, Tz * H * 4), span(z, Tz * H * 4), span(q, Tz * H),
+                      span(d, Tz * (H / 32) * 4)};
+  for (int o = 0; o < 7; ++o) {
+    for (const Span& i : in)
+      if (overlaps(out[o], i)) return MHC_EOVERLAP;
+    for (int p = o + 1; p < 7; ++p)
+      if (overlaps(out[o], out[p])) return MHC_EOVERLAP;
+  }
+  return MHC_OK;
+}
+
+int mhc_site_pre_zq8(const float* x, const float* fn_w, const float* scale, const float* base,
+                     const float* nw, int T, int streams, int hidden, int iters, float eps,
+                     float norm_eps, float* pre, float* post, float* comb, float* y, float* z,
+                     signed char* q, float* d, void* stream) {
+  int rc = mhc_site_pre_zq8_check(x, fn_w, scale, base, nw, T, streams, hidden, iters, eps,
+                                  norm_eps, pre, post, comb, y, z, q, d);
+  if (rc || T == 0) return rc;
+  if ((rc = mhc_site_pre(x, fn_w, scale, base, T, streams, hidden, iters, eps, pre, post, comb,
+                         y, stream)))
+    return rc;
+  if (mhc::launch_zq8(y, nw, T, hidden, norm_eps, z, q, d, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return MHC_EHIP;
+  return MHC_OK;
+}
+
 int mhc_site_post(const float* x, const float* f, const float* post, const float* comb, int T,
                   int streams, int hidden, float* x_out, void* stream) {
   int rc = mhc_site_post_check(x, f, post, comb, T, streams, hidden, x_out);

@@ -46,6 +46,12 @@ hipError_t launch_decode4_pre(const float* x, const float* fn_w, const float* sc
                               int G, int chunks_per_range, float* part, unsigned int* counter,
                               float* pre, float* post, float* comb, float* y, hipStream_t st);
 
+// Branch-input epilogue: z = RMS-norm(y) * nw and its q8 codes / block scales,
+// one block per token; H % 32 == 0 and H <= 8192 (zq8_supported).
+bool zq8_supported(int H);
+hipError_t launch_zq8(const float* y, const float* nw, int T, int H, float norm_eps, float* z,
+                      signed char* q, float* d, hipStream_t st);
+
 // Post mix.
 hipError_t launch_post(const float* x, const float* f, const float* post, const float* comb,
                        int T, int S, int H, float* x_out, hipStream_t st);

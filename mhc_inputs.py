@@ -76,3 +76,11 @@ def make_random_shape(T: int, S: int, H: int, seed: int):
     """Same distributions as the configs, for an arbitrary (T, S, H)."""
     cfg = SiteConfig("adhoc", 1000 + S * 131 + H, T, S, H)
     return make_site(cfg, T=T, seed=seed)
+
+
+def make_norm_weight(H: int, seed: int = SEED):
+    """The branch-input norm weight nw [H] (float32): 1 + U[-0.5, 0.5), seeded by
+    SeedSequence([seed, 77, H]); the pages' gate draws it as one plus a small
+    random vector."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 77, H])))
+    return (1.0 + g.uniform(-0.5, 0.5, size=H)).astype(np.float32)

@@ -122,3 +122,39 @@ def test_invalid_call_returns_before_any_gpu_work(lib):
     assert lib.mhc_site_pre(None, None, None, None, 4, 4, 128, 0, 1e-6,
                             None, None, None, None, None) == EINVAL
     assert lib.mhc_site_post(None, None, None, None, 4, 9, 128, None, None) == EUNSUP
+
+
+def _zq8_addrs(T, S, H):
+    R = (2 + S) * S
+    sizes = [T * S * H, R * S * H, 4, R, H, T * S, T * S, T * S * S, T * H, T * H, T * H, T * H // 32 + 1]
+    out, a = [], 1 << 30
+    for n in sizes:
+        out.append(a)
+        a += ((n * 4 + 255) // 256) * 256 + 256
+    return out
+
+
+def test_zq8_check(lib):
+    T, S, H = 8, 4, 4096
+    a = _zq8_addrs(T, S, H)
+    x, w, sc, b, nw, pre, post, comb, y, z, q, d = a
+    ok = mhc.site_pre_zq8_check(x, w, sc, b, nw, T, S, H, 20, 1e-6, 1e-5, pre, post, comb, y, z, q, d)
+    assert ok == OK
+    # hidden must be a multiple of 32 (the q8 block)
+    assert mhc.site_pre_zq8_check(x, w, sc, b, nw, T, S, 4100, 20, 1e-6, 1e-5, pre, post, comb, y,
+                                  z, q, d) == EALIGN
+    assert mhc.site_pre_zq8_check(x, w, sc, b, nw, T, S, 16384, 20, 1e-6, 1e-5, pre, post, comb, y,
+                                  z, q, d) == EUNSUP
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert mhc.site_pre_zq8_check(x, w, sc, b, nw, T, S, H, 20, 1e-6, bad, pre, post, comb, y,
+                                      z, q, d) == EINVAL
+    assert mhc.site_pre_zq8_check(x, w, sc, b, 0, T, S, H, 20, 1e-6, 1e-5, pre, post, comb, y, z,
+                                  q, d) == EINVAL
+    # z written over y, q over the norm weight: refused
+    assert mhc.site_pre_zq8_check(x, w, sc, b, nw, T, S, H, 20, 1e-6, 1e-5, pre, post, comb, y, y,
+                                  q, d) == EOVERLAP
+    assert mhc.site_pre_zq8_check(x, w, sc, b, nw, T, S, H, 20, 1e-6, 1e-5, pre, post, comb, y, z,
+                                  nw, d) == EOVERLAP
+    # the pre-site checks still apply
+    assert mhc.site_pre_zq8_check(x, w, sc, b, nw, T, S, H, 0, 1e-6, 1e-5, pre, post, comb, y, z,
+                                  q, d) == EINVAL
