@@ -109,14 +109,22 @@ def time_site(mhc, torch, t, c, out_pre, out_x, steps, warmup):
     return total_ms / steps, pre_ms, post_ms, wall
 
 
-def time_decode(mhc, torch, t, c, out_pre, out_x, sites, graph_sites=50):
+def time_decode(mhc, torch, t, c, out_pre, out_x, sites, graph_sites=50, zq8=None):
     """Decode sites back to back on one stream: (a) eager calls, no per-call events
     (host launch cost included); (b) a HIP graph of `graph_sites` sites replayed,
     which leaves only device time and the gaps between kernels.  Returns µs/site
-    for both."""
+    for both.  With zq8=(nw, norm_eps, out7) the pre half is the call with the
+    branch-input epilogue."""
     def site():
-        mhc.site_pre(t["x"], t["fn_w"], t["scale"], t["base"], c.iters, c.eps, out=out_pre)
-        mhc.site_post(t["x"], t["f"], out_pre[1], out_pre[2], out=out_x)
+        if zq8 is None:
+            mhc.site_pre(t["x"], t["fn_w"], t["scale"], t["base"], c.iters, c.eps, out=out_pre)
+            po, pc = out_pre[1], out_pre[2]
+        else:
+            nw, neps, o7 = zq8
+            mhc.site_pre_zq8(t["x"], t["fn_w"], t["scale"], t["base"], nw, c.iters, c.eps, neps,
+                             out=o7)
+            po, pc = o7[1], o7[2]
+        mhc.site_post(t["x"], t["f"], po, pc, out=out_x)
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -148,6 +156,38 @@ def time_decode(mhc, torch, t, c, out_pre, out_x, sites, graph_sites=50):
     torch.cuda.synchronize()
     graph_us = a.elapsed_time(b) * 1e3 / (reps * graph_sites)
     return eager_us, graph_us
+
+
+def time_pre_zq8(mhc, torch, t, c, nw, norm_eps, out7, steps, warmup):
+    """Mean µs of the pre call with the branch-input epilogue, back to back on the
+    current stream (HIP events around each call)."""
+    def call():
+        mhc.site_pre_zq8(t["x"], t["fn_w"], t["scale"], t["base"], nw, c.iters, c.eps, norm_eps,
+                         out=out7)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / steps * 1e3
+
+
+def zq8_bytes(T, H):
+    """Algorithmic HBM bytes of the epilogue on its own: read y and nw; write z,
+    the int8 codes and one fp32 scale per 32 columns."""
+    return 4 * T * H + 4 * H + 4 * T * H + T * H + 4 * (T * H // 32)
+
+
+def alloc_zq8(T, S, H, torch):
+    e = lambda *s, dt=torch.float32: torch.empty(s, device="cuda", dtype=dt)  # noqa: E731
+    return (e(T, S), e(T, S), e(T, S, S), e(T, H), e(T, H), e(T, H, dt=torch.int8),
+            e(T, H // 32))
 
 
 def cpu_baseline(c, d, cpu_seconds=15.0, max_wall=30.0):
@@ -320,6 +360,20 @@ def main():
     d_eager_us, d_graph_us = time_decode(mhc, torch, td, cd, dpre, dx, n)
     pre1, post1 = algorithmic_bytes(cd.T, cd.S, cd.H)
 
+    # ---- branch-input epilogue (RMS norm of y with a weight, q8 codes): the pre
+    # call with it, against the same call without it
+    from mhc_inputs import make_norm_weight
+    norm_eps = 1e-5
+    nw_p = torch.from_numpy(make_norm_weight(c.H, 1)).cuda()
+    o7 = alloc_zq8(c.T, c.S, c.H, torch)
+    zq_pre_us = time_pre_zq8(mhc, torch, t, c, nw_p, norm_eps, o7, args.steps, args.warmup)
+    nw_d = torch.from_numpy(make_norm_weight(cd.H, 1)).cuda()
+    o7d = alloc_zq8(cd.T, cd.S, cd.H, torch)
+    zq_d_eager_us, zq_d_graph_us = time_decode(mhc, torch, td, cd, dpre, dx, n,
+                                               zq8=(nw_d, norm_eps, o7d))
+    epi_b = zq8_bytes(c.T, c.H)
+    epi_us = zq_pre_us - pre_ms * 1e3
+
     # ---- CPU oracle baseline (host cores, bounded sample)
     cpu = None if args.no_cpu_baseline else cpu_baseline(c, d)
 
@@ -351,6 +405,15 @@ def main():
                               "kernels); eager: the same sites as plain calls, host launch "
                               "included",
                       "algorithmic_bytes_per_site": pre1 + post1},
+        "epilogue_zq8": {
+            "prefill_pre_zq8_us": round(zq_pre_us, 2),
+            "prefill_added_us": round(epi_us, 2),
+            "prefill_algorithmic_bytes_alone": epi_b,
+            "decode_t1_us_per_site": round(zq_d_graph_us, 3),
+            "decode_t1_eager_us_per_site": round(zq_d_eager_us, 3),
+            "note": "the pre call with the epilogue (z = RMS-norm(y) * nw, q8 codes and "
+                    "scales); added_us = its time minus pre_us; decode sites as in decode_t1 "
+                    "with the epilogue in the pre call"},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

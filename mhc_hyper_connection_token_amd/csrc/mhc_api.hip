@@ -175,44 +175,72 @@ int mhc_site_post_check(const float* x, const float* f, const float* post, const
   return MHC_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// The pre chain for checked arguments.  With zq, the branch-input epilogue runs
+// in the tail of the fused and single-launch decode kernels where they support
+// it, otherwise as its own launch after the chain.
+int site_pre_run(const float* x, const float* fn_w, const float* scale, const float* base, int T,
+                 int S, int H, int iters, float eps, float* pre, float* post, float* comb,
+                 float* y, const mhc::Zq8Out* zq, hipStream_t st) {
+  int rc;
+  const int n = S * H, R = (2 + S) * S;
+  bool zq_done = false;
+  if (T >= kFusedMinTokens && mhc::fused_supported(S, H)) {
+    // Large batches with a slab that fits on chip: x read once.
+    Scratch sc;
+    if ((rc = get_scratch(mhc::fused_pack_bytes(S, H), &sc))) return rc;
+    if (mhc::launch_fused_pre(x, fn_w, scale, base, T, S, H, iters, eps, pre, post, comb, y,
+                              sc.general, zq, st) != hipSuccess)
+      return MHC_EHIP;
+    zq_done = true;
+  } else {
+    const PrePlan p = plan_pre(T, S, H);
+    Scratch sc;
+    if ((rc = get_scratch(p.part_floats * sizeof(float), &sc))) return rc;
+    float* part = sc.general;
+    hipError_t e;
+    if (T <= 2) {
+      // decode sizes: one launch; the block that draws the last ticket finishes
+      if (mhc::decode4_supported(T, S, p.G)) {
+        const bool fuse = zq && mhc::decode4_zq8_supported(T, H);
+        e = mhc::launch_decode4_pre(x, fn_w, scale, base, T, S, H, iters, eps, p.G, p.cpr, part,
+                                    sc.counter, pre, post, comb, y, fuse ? zq : nullptr, st);
+        zq_done = fuse;
+      } else {
+        e = mhc::launch_decode_pre(x, fn_w, scale, base, T, S, H, iters, eps, p.G, p.cpr, part,
+                                   sc.counter, pre, post, comb, y, st);
+      }
+    } else {
+      e = (T <= 16 && S <= 4)
+              ? mhc::launch_small_partials(x, fn_w, T, S, H, p.G, p.cpr, part, st)
+              : mhc::launch_partials(x, fn_w, T, n, R, p.ntt, p.G, p.cpr, part, st);
+      if (e == hipSuccess)
+        e = mhc::launch_finish(x, part, p.G, T, S, H, scale, base, iters, eps, pre, post, comb,
+                               y, st);
+    }
+    if (e != hipSuccess) return MHC_EHIP;
+  }
+  if (zq && !zq_done &&
+      mhc::launch_zq8(y, zq->nw, T, H, zq->norm_eps, zq->z, zq->q, zq->d, st) != hipSuccess)
+    return MHC_EHIP;
+  return MHC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int mhc_site_pre(const float* x, const float* fn_w, const float* scale, const float* base, int T,
                  int streams, int hidden, int iters, float eps, float* pre, float* post,
                  float* comb, float* y, void* stream) {
   int rc = mhc_site_pre_check(x, fn_w, scale, base, T, streams, hidden, iters, eps, pre, post,
                               comb, y);
   if (rc || T == 0) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const int S = streams, H = hidden, n = S * H, R = (2 + S) * S;
-  if (T >= kFusedMinTokens && mhc::fused_supported(S, H)) {
-    // Large batches with a slab that fits on chip: x read once.
-    Scratch sc;
-    if ((rc = get_scratch(mhc::fused_pack_bytes(S, H), &sc))) return rc;
-    if (mhc::launch_fused_pre(x, fn_w, scale, base, T, S, H, iters, eps, pre, post, comb, y,
-                              sc.general, st) != hipSuccess)
-      return MHC_EHIP;
-    return MHC_OK;
-  }
-  const PrePlan p = plan_pre(T, S, H);
-  Scratch sc;
-  if ((rc = get_scratch(p.part_floats * sizeof(float), &sc))) return rc;
-  float* part = sc.general;
-  if (T <= 2) {
-    // decode sizes: one launch; the block that draws the last ticket finishes
-    hipError_t e = mhc::decode4_supported(T, S, p.G)
-                       ? mhc::launch_decode4_pre(x, fn_w, scale, base, T, S, H, iters, eps, p.G,
-                                                 p.cpr, part, sc.counter, pre, post, comb, y, st)
-                       : mhc::launch_decode_pre(x, fn_w, scale, base, T, S, H, iters, eps, p.G,
-                                                p.cpr, part, sc.counter, pre, post, comb, y, st);
-    return e == hipSuccess ? MHC_OK : MHC_EHIP;
-  }
-  const hipError_t pe = (T <= 16 && S <= 4)
-                           ? mhc::launch_small_partials(x, fn_w, T, S, H, p.G, p.cpr, part, st)
-                           : mhc::launch_partials(x, fn_w, T, n, R, p.ntt, p.G, p.cpr, part, st);
-  if (pe != hipSuccess) return MHC_EHIP;
-  if (mhc::launch_finish(x, part, p.G, T, S, H, scale, base, iters, eps, pre, post, comb, y,
-                         st) != hipSuccess)
-    return MHC_EHIP;
-  return MHC_OK;
+  return site_pre_run(x, fn_w, scale, base, T, streams, hidden, iters, eps, pre, post, comb, y,
+                      nullptr, static_cast<hipStream_t>(stream));
 }
 
 int mhc_site_pre_zq8_check(const float* x, const float* fn_w, const float* scale,
@@ -258,13 +286,9 @@ int mhc_site_pre_zq8(const float* x, const float* fn_w, const float* scale, cons
   int rc = mhc_site_pre_zq8_check(x, fn_w, scale, base, nw, T, streams, hidden, iters, eps,
                                   norm_eps, pre, post, comb, y, z, q, d);
   if (rc || T == 0) return rc;
-  if ((rc = mhc_site_pre(x, fn_w, scale, base, T, streams, hidden, iters, eps, pre, post, comb,
-                         y, stream)))
-    return rc;
-  if (mhc::launch_zq8(y, nw, T, hidden, norm_eps, z, q, d, static_cast<hipStream_t>(stream)) !=
-      hipSuccess)
-    return MHC_EHIP;
-  return MHC_OK;
+  const mhc::Zq8Out zq{nw, norm_eps, z, q, d};
+  return site_pre_run(x, fn_w, scale, base, T, streams, hidden, iters, eps, pre, post, comb, y,
+                      &zq, static_cast<hipStream_t>(stream));
 }
 
 int mhc_site_post(const float* x, const float* f, const float* post, const float* comb, int T,

@@ -14,7 +14,9 @@
 // that draws the last ticket requests every partial and, right behind them,
 // the collapse operands, adds the partials, and then splits: wave 0 runs the
 // gates and the Sinkhorn while the other waves compute the pre gates
-// themselves and collapse.  It resets the counter for the next call.
+// themselves and collapse.  It resets the counter for the next call.  With ZQ
+// the collapse keeps y in registers and the block then runs the branch-input
+// epilogue (z = RMS-norm(y) * nw, q8 codes and scales) behind one more barrier.
 //
 // S > 4 (decode_pre_kernel): the same ticket scheme with the 256-thread
 // reduction of the finish kernel.
@@ -123,15 +125,19 @@ __global__ __launch_bounds__(256) void decode_pre_kernel(
   }
 }
 
-template <int RPT>
+constexpr int kD4Batch = 6;  // collapse quads in flight per collapse thread
+constexpr int kD4ZqBatches = 2;  // collapse batches whose y the epilogue keeps in registers
+
+template <int RPT, bool ZQ>
 __global__ __launch_bounds__(256) void decode4_pre_kernel(
     const float* __restrict__ x, const float* __restrict__ fn_w, const float* __restrict__ scale,
     const float* __restrict__ base, int T, int S, int H, int iters, float eps,
     int chunks_per_range, float* __restrict__ part, unsigned int* __restrict__ counter,
     float* __restrict__ pre, float* __restrict__ post, float* __restrict__ comb,
-    float* __restrict__ y) {
-  constexpr int KB = 6;  // collapse quads in flight per collapse thread
+    float* __restrict__ y, Zq8Out zq) {
+  constexpr int KB = kD4Batch;
   __shared__ float red256[2][256];
+  __shared__ float zred[4][2];
   __shared__ float m_raw[2][32];
   __shared__ float params[3 + 24];
   __shared__ int is_last;
@@ -180,7 +186,9 @@ __global__ __launch_bounds__(256) void decode4_pre_kernel(
   const int HQ = H >> 2;
   const int total = T * HQ;
   float4 xq[KB][4];
-  auto load_batch = [&](int i0) {
+  float4 wk[ZQ ? kD4ZqBatches : 1][KB];  // epilogue weight quads of the kept batches
+  const float4* nw4 = reinterpret_cast<const float4*>(zq.nw);
+  auto load_batch = [&](int i0, int bb) {
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
       const int idx = i0 + k * nct;
@@ -191,8 +199,16 @@ __global__ __launch_bounds__(256) void decode4_pre_kernel(
       for (int c = 0; c < 4; ++c)
         if (c < S) xq[k][c] = xt[(size_t)c * HQ];
     }
+    if constexpr (ZQ) {  // behind the x quads, so the collapse does not wait for them
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int idx = i0 + k * nct;
+        const int ic = idx < total ? idx : 0;
+        wk[bb][k] = nw4[ic - (ic / HQ) * HQ];
+      }
+    }
   };
-  if (wave >= 1) load_batch(ct);
+  if (wave >= 1) load_batch(ct, 0);
   __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
@@ -215,7 +231,7 @@ __global__ __launch_bounds__(256) void decode4_pre_kernel(
   if (wave == 0) {
     gates_wave<4, false>(&m_raw[0][0], 32, T, S, n, params, iters, eps, true, pre, post, comb,
                          nullptr);
-    return;
+    if constexpr (!ZQ) return;  // with the epilogue, wave 0 meets the others at its barrier
   }
 
   // collapse: y[t, i] = sum_c pre[t, c] * x[t, c, i]
@@ -225,16 +241,78 @@ __global__ __launch_bounds__(256) void decode4_pre_kernel(
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       pc[t][c] = (t < T && c < S) ? pre_gate(m_raw[t], c, R, n, eps, params) : 0.f;
-  if (ct < T * S) pre[ct] = pre_gate(m_raw[ct / S], ct % S, R, n, eps, params);
-  for (int i0 = ct; i0 < total; i0 += KB * nct) {
-    if (i0 != ct) load_batch(i0);
+  if (wave != 0 && ct < T * S) pre[ct] = pre_gate(m_raw[ct / S], ct % S, R, n, eps, params);
+  if constexpr (!ZQ) {
+    for (int i0 = ct; i0 < total; i0 += KB * nct) {
+      if (i0 != ct) load_batch(i0, 0);
 #pragma unroll
-    for (int k = 0; k < KB; ++k) {
-      const int idx = i0 + k * nct;
-      if (idx < total) {
-        const int t = idx / HQ, qq = idx - t * HQ;
-        reinterpret_cast<float4*>(y + (size_t)t * H)[qq] =
-            collapse4<4>(t == 0 ? pc[0] : pc[1], xq[k], S);
+      for (int k = 0; k < KB; ++k) {
+        const int idx = i0 + k * nct;
+        if (idx < total) {
+          const int t = idx / HQ, qq = idx - t * HQ;
+          reinterpret_cast<float4*>(y + (size_t)t * H)[qq] =
+              collapse4<4>(t == 0 ? pc[0] : pc[1], xq[k], S);
+        }
+      }
+    }
+  } else {
+    // Collapse with y kept in registers (T*H/4 <= kD4ZqBatches*KB*192 quads),
+    // then the branch-input epilogue.  [T][H] outputs are indexed by the
+    // flattened quad idx = t*H/4 + quad; H % 32 == 0 puts the 8 quads of a
+    // 32-entry block in 8 neighbouring lanes (idx = ct mod 8) of one token,
+    // wholly before or past the end.
+    float4 yk[kD4ZqBatches][KB];
+    float ys[2] = {0.f, 0.f};
+    if (wave != 0) {
+#pragma unroll
+      for (int bb = 0; bb < kD4ZqBatches; ++bb) {
+        if (bb * KB * nct < total) {  // the same in every thread
+          const int i0 = ct + bb * KB * nct;
+          if (bb != 0) load_batch(i0, bb);
+#pragma unroll
+          for (int k = 0; k < KB; ++k) {
+            const int idx = i0 + k * nct;
+            const int ic = idx < total ? idx : 0;
+            const int t = ic / HQ;
+            yk[bb][k] = collapse4<4>(t == 0 ? pc[0] : pc[1], xq[k], S);
+            if (idx < total) {
+              reinterpret_cast<float4*>(y)[idx] = yk[bb][k];
+              if (t == 0)
+                ys[0] = sq4(yk[bb][k], ys[0]);
+              else
+                ys[1] = sq4(yk[bb][k], ys[1]);
+            }
+          }
+        }
+      }
+      // sums of squares of y per token: each wave, then waves 1, 2, 3 in order
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float sw = sum_wave(ys[t]);
+        if ((tid & (kWave - 1)) == 0) zred[wave][t] = sw;
+      }
+    }
+    __syncthreads();  // all four waves (wave 0 once its Sinkhorn is done)
+    if (wave == 0) return;
+    const float r0 = zq8_rinv(zred[1][0] + zred[2][0] + zred[3][0], H, zq.norm_eps);
+    const float r1 = zq8_rinv(zred[1][1] + zred[2][1] + zred[3][1], H, zq.norm_eps);
+#pragma unroll
+    for (int bb = 0; bb < kD4ZqBatches; ++bb) {
+      if (bb * KB * nct < total) {
+        const int i0 = ct + bb * KB * nct;
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+          const int idx = i0 + k * nct;
+          const int ic = idx < total ? idx : 0;
+          const float4 o = zq8_norm(yk[bb][k], ic < HQ ? r0 : r1, wk[bb][k]);
+          float db;
+          const char4 cq = zq8_codes(o, &db);
+          if (idx < total) {
+            reinterpret_cast<float4*>(zq.z)[idx] = o;
+            reinterpret_cast<char4*>(zq.q)[idx] = cq;
+            if ((idx & 7) == 0) zq.d[idx >> 3] = db;
+          }
+        }
       }
     }
   }
@@ -245,17 +323,29 @@ bool decode4_supported(int T, int S, int G) {
   return T >= 1 && T <= 2 && S >= 1 && S <= 4 && G >= 1 && G <= 16 * (256 / RP);
 }
 
+bool decode4_zq8_supported(int T, int H) {
+  return H % 32 == 0 && (long)T * (H / 4) <= (long)kD4ZqBatches * kD4Batch * 3 * kWave;
+}
+
 hipError_t launch_decode4_pre(const float* x, const float* fn_w, const float* scale,
                               const float* base, int T, int S, int H, int iters, float eps,
                               int G, int chunks_per_range, float* part, unsigned int* counter,
-                              float* pre, float* post, float* comb, float* y, hipStream_t st) {
+                              float* pre, float* post, float* comb, float* y, const Zq8Out* zq,
+                              hipStream_t st) {
   if (!decode4_supported(T, S, G)) return hipErrorInvalidValue;
+  if (zq && !decode4_zq8_supported(T, H)) return hipErrorInvalidValue;
+  const Zq8Out zv = zq ? *zq : Zq8Out{nullptr, 0.f, nullptr, nullptr, nullptr};
   const int rpt = small_rows_per_thread(S);
 #define MHC_D4(RP_)                                                                           \
   if (rpt == RP_) {                                                                            \
-    hipLaunchKernelGGL((decode4_pre_kernel<RP_>), dim3(G), dim3(256), 0, st, x, fn_w, scale,   \
-                       base, T, S, H, iters, eps, chunks_per_range, part, counter, pre, post,   \
-                       comb, y);                                                               \
+    if (zq)                                                                                    \
+      hipLaunchKernelGGL((decode4_pre_kernel<RP_, true>), dim3(G), dim3(256), 0, st, x, fn_w,  \
+                         scale, base, T, S, H, iters, eps, chunks_per_range, part, counter,    \
+                         pre, post, comb, y, zv);                                              \
+    else                                                                                       \
+      hipLaunchKernelGGL((decode4_pre_kernel<RP_, false>), dim3(G), dim3(256), 0, st, x, fn_w, \
+                         scale, base, T, S, H, iters, eps, chunks_per_range, part, counter,    \
+                         pre, post, comb, y, zv);                                              \
     return hipGetLastError();                                                                  \
   }
   MHC_D4(1) MHC_D4(2) MHC_D4(4)

@@ -65,6 +65,11 @@ __device__ __forceinline__ float sum_row16(float v) {
   return v;
 }
 
+// Sum over the whole wavefront; read one lane (lane 0).
+__device__ __forceinline__ float sum_wave(float v) {
+  return swap32_sum(swap16_sum(sum_row16(v)));
+}
+
 // ---------------------------------------------------------------- Sinkhorn
 // Two lane layouts for the S x S block (entries outside S x S hold 0 and stay 0,
 // so padded sums equal the true sums):
@@ -238,6 +243,40 @@ __device__ __forceinline__ float4 collapse4(const float* pre, const float4* xs, 
     }
   }
   return o;
+}
+
+// ---------------------------------------------------------------- branch-input epilogue
+// (hc_fused_gate.rs page, the v4z timing block: the norm and the q8 encoding of
+// the branch input.)  z = y * r * w per entry, r = 1/sqrt(mean y^2 + norm_eps);
+// per block of 32 consecutive entries d = max|z| / 127 and codes round(z * (1/d))
+// with ties away from zero (d = 0, codes 0 for an all-zero block).  The division
+// and the reciprocal are IEEE fp32 and the rounding is roundf, so codes and scale
+// are a pure function of the fp32 z that is written.
+__device__ __forceinline__ float zq8_rinv(float ss, int H, float norm_eps) {
+  return __builtin_amdgcn_rsqf(fmaf(ss, 1.0f / (float)H, norm_eps));
+}
+__device__ __forceinline__ float4 zq8_norm(float4 y, float r, float4 w) {
+  return make_float4(y.x * r * w.x, y.y * r * w.y, y.z * r * w.z, y.w * r * w.w);
+}
+__device__ __forceinline__ float sq4(float4 v, float acc) {
+  acc = fmaf(v.x, v.x, acc);
+  acc = fmaf(v.y, v.y, acc);
+  acc = fmaf(v.z, v.z, acc);
+  return fmaf(v.w, v.w, acc);
+}
+// q8 of one quad of z whose 32-entry block is held by the eight neighbouring
+// lanes of an aligned 8-lane group (lane bits 0-2), all eight calling together.
+// Returns the codes; *db receives the block scale (the same in all 8 lanes).
+__device__ __forceinline__ char4 zq8_codes(float4 o, float* db) {
+  float a = fmaxf(fmaxf(fabsf(o.x), fabsf(o.y)), fmaxf(fabsf(o.z), fabsf(o.w)));
+  a = fmaxf(a, dpp<0xB1>(a));   // quad_perm [1,0,3,2]
+  a = fmaxf(a, dpp<0x4E>(a));   // quad_perm [2,3,0,1]
+  a = fmaxf(a, dpp<0x141>(a));  // half-row mirror: the other quad
+  const float d = a / 127.0f;
+  const float id = d != 0.0f ? 1.0f / d : 0.0f;
+  *db = d;
+  return make_char4((signed char)roundf(o.x * id), (signed char)roundf(o.y * id),
+                    (signed char)roundf(o.z * id), (signed char)roundf(o.w * id));
 }
 
 }  // namespace mhc

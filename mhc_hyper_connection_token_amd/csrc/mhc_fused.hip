@@ -18,7 +18,10 @@
 // moved into the A-operand lanes with ds_bpermute.  Every tile streams the whole
 // packed weight from L2 (1.5 MiB at 4 x 4096), which bounds the kernel by the
 // CU's L1 fill rate; one weight chunk is prefetched ahead of the MFMAs.
-#include "mhc_device.h"
+//
+// With ZQ the tail also runs the branch-input epilogue (z = RMS-norm(y) * nw,
+// its q8 codes and scales) from the y still in registers: one more barrier for
+// the per-token sum of squares, and y is never read back.
 #include "mhc_device.h"
 #include "mhc_kernels.h"
 
@@ -51,12 +54,12 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const float* __restric
                   : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-template <int S, int CPW, int WD>
+template <int S, int CPW, int WD, bool ZQ>
 __global__ __launch_bounds__(512) void fused_pre_kernel(
     const float* __restrict__ x, const float4* __restrict__ wpack,
     const float* __restrict__ scale, const float* __restrict__ base, int T, int H, int iters,
     float eps, float* __restrict__ pre, float* __restrict__ post, float* __restrict__ comb,
-    float* __restrict__ y) {
+    float* __restrict__ y, Zq8Out zq) {
   constexpr int R = (2 + S) * S;
   constexpr int RG = (R + 3) / 4;  // weight-row groups of 4
   constexpr int NW = 8;
@@ -66,6 +69,7 @@ __global__ __launch_bounds__(512) void fused_pre_kernel(
   __shared__ float mr[4][R + 1];
   __shared__ float pre_lds[4 * 8];
   __shared__ float params[3 + R];
+  __shared__ float zred[ZQ ? NW : 1][4];
 
   stage_site_params(scale, base, R, params);
   const int lane = threadIdx.x & (kWave - 1);
@@ -180,7 +184,52 @@ __global__ __launch_bounds__(512) void fused_pre_kernel(
   __syncthreads();
 
   // ---- collapse from registers (memory layout: token tq, columns 4*bq..)
-  if (tok_ok) {
+  if constexpr (ZQ) {
+    // Collapse and branch-input epilogue.  Every lane computes (lanes of tokens
+    // past T on token 0's data, never stored), because the block maximum of a
+    // 32-entry block is a butterfly over the 8 lanes holding it (bq bits 0-2;
+    // H % 32 == 0, so a block is wholly inside or outside the hidden size).
+    float pc[S];
+#pragma unroll
+    for (int c = 0; c < S; ++c) pc[c] = pre_lds[tq * 8 + c];
+    float4 yv[CPW];
+    float ys = 0.f;
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      const int h = 64 * (wave * CPW + u) + 4 * bq;
+      float4 xs[S];
+#pragma unroll
+      for (int c = 0; c < S; ++c) xs[c] = xr[c * CPW + u];
+      yv[u] = collapse4<S>(pc, xs, S);
+      if (h < H) {
+        ys = sq4(yv[u], ys);
+        if (tok_ok) nt_store4(y + (size_t)tok * H + h, yv[u]);
+      }
+    }
+    // sum of squares of the token's y: its 16 lanes, then the 8 waves in order
+    ys = sum_row16(ys);
+    if ((lane & 15) == 0) zred[wave][tq] = ys;
+    __syncthreads();
+    float ssy = zred[0][tq];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) ssy += zred[ww][tq];
+    const float r = zq8_rinv(ssy, H, zq.norm_eps);
+    const size_t row = (size_t)(tok_ok ? tok : 0) * H;
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      const int h = 64 * (wave * CPW + u) + 4 * bq;
+      const bool hin = h < H;
+      const float4 w = *reinterpret_cast<const float4*>(zq.nw + (hin ? h : 0));
+      const float4 o = zq8_norm(yv[u], r, w);
+      float db;
+      const char4 cq = zq8_codes(o, &db);
+      if (tok_ok && hin) {
+        nt_store4(zq.z + row + h, o);
+        *reinterpret_cast<char4*>(zq.q + row + h) = cq;
+        if ((bq & 7) == 0) zq.d[(row + h) >> 5] = db;
+      }
+    }
+  } else if (tok_ok) {
     float pc[S];
 #pragma unroll
     for (int c = 0; c < S; ++c) pc[c] = pre_lds[tq * 8 + c];
@@ -220,8 +269,9 @@ size_t fused_pack_bytes(int S, int H) {
 hipError_t launch_fused_pre(const float* x, const float* fn_w, const float* scale,
                             const float* base, int T, int S, int H, int iters, float eps,
                             float* pre, float* post, float* comb, float* y, float* wpack,
-                            hipStream_t st) {
-  if (!fused_supported(S, H)) return hipErrorInvalidValue;
+                            const Zq8Out* zq, hipStream_t st) {
+  if (!fused_supported(S, H) || (zq && H % 32 != 0)) return hipErrorInvalidValue;
+  const Zq8Out zv = zq ? *zq : Zq8Out{nullptr, 0.f, nullptr, nullptr, nullptr};
   const int cpw = fused_cpw(H);
   const int total = (int)(fused_pack_bytes(S, H) / sizeof(float4));
   float4* pk = reinterpret_cast<float4*>(wpack);
@@ -230,8 +280,12 @@ hipError_t launch_fused_pre(const float* x, const float* fn_w, const float* scal
   if (S == SS && cpw == CC) {                                                                 \
     hipLaunchKernelGGL((pack_weight_kernel<SS, CC>), dim3((total + 255) / 256), dim3(256), 0, \
                        st, fn_w, H, pk);                                                      \
-    hipLaunchKernelGGL((fused_pre_kernel<SS, CC, 1>), grid, dim3(512), 0, st, x, pk, scale,      \
-                       base, T, H, iters, eps, pre, post, comb, y);                           \
+    if (zq)                                                                                   \
+      hipLaunchKernelGGL((fused_pre_kernel<SS, CC, 1, true>), grid, dim3(512), 0, st, x, pk,   \
+                         scale, base, T, H, iters, eps, pre, post, comb, y, zv);              \
+    else                                                                                      \
+      hipLaunchKernelGGL((fused_pre_kernel<SS, CC, 1, false>), grid, dim3(512), 0, st, x, pk,  \
+                         scale, base, T, H, iters, eps, pre, post, comb, y, zv);              \
     return hipGetLastError();                                                                 \
   }
   MHC_FU(1, 1) MHC_FU(1, 2) MHC_FU(1, 4) MHC_FU(1, 8) MHC_FU(1, 16)

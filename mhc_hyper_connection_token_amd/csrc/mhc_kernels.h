@@ -4,6 +4,16 @@
 
 namespace mhc {
 
+// Operands of the branch-input epilogue run in a pre kernel's tail: z = RMS-norm
+// of y times nw, its int8 codes q and per-32 scales d (token-major, like y).
+struct Zq8Out {
+  const float* nw;
+  float norm_eps;
+  float* z;
+  signed char* q;
+  float* d;
+};
+
 // Split-K partial mixes + sums of squares: part[G][T][R+1].
 // ntt = token tiles of 16 per block (1, 2 or 4, depending on the row-tile count).
 hipError_t launch_partials(const float* x, const float* fn_w, int T, int n, int R, int ntt,
@@ -23,12 +33,13 @@ hipError_t launch_finish(const float* x, const float* part, int G, int T, int S,
 // Token-tiled fused pre chain (slab held on chip), for S <= 4 and H up to a
 // register budget; fused_supported() says whether a shape qualifies.
 // wpack: scratch of fused_pack_bytes(S, H) bytes for the weight in operand order.
+// With zq non-null (H % 32 == 0) the kernel also writes the branch-input epilogue.
 bool fused_supported(int S, int H);
 size_t fused_pack_bytes(int S, int H);
 hipError_t launch_fused_pre(const float* x, const float* fn_w, const float* scale,
                             const float* base, int T, int S, int H, int iters, float eps,
                             float* pre, float* post, float* comb, float* y, float* wpack,
-                            hipStream_t st);
+                            const Zq8Out* zq, hipStream_t st);
 
 // Single-launch pre chain for T <= 2: split-K partials into `part`, last block
 // (ticket on `counter`, which must be zero on entry and is zero again on exit)
@@ -39,12 +50,16 @@ hipError_t launch_decode_pre(const float* x, const float* fn_w, const float* sca
                              float* pre, float* post, float* comb, float* y, hipStream_t st);
 
 // Single-launch pre chain for T <= 2 and S <= 4 (same ticket contract), with
-// the collapse operands requested while the partials are being added.
+// the collapse operands requested while the partials are being added.  With zq
+// non-null the last block also writes the branch-input epilogue; that needs
+// decode4_zq8_supported(T, H).
 bool decode4_supported(int T, int S, int G);
+bool decode4_zq8_supported(int T, int H);
 hipError_t launch_decode4_pre(const float* x, const float* fn_w, const float* scale,
                               const float* base, int T, int S, int H, int iters, float eps,
                               int G, int chunks_per_range, float* part, unsigned int* counter,
-                              float* pre, float* post, float* comb, float* y, hipStream_t st);
+                              float* pre, float* post, float* comb, float* y, const Zq8Out* zq,
+                              hipStream_t st);
 
 // Branch-input epilogue: z = RMS-norm(y) * nw and its q8 codes / block scales,
 // one block per token; H % 32 == 0 and H <= 8192 (zq8_supported).

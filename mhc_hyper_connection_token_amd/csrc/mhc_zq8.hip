@@ -5,10 +5,11 @@
 //   z[t,i] = y[t,i] * nw[i] * r,   r = 1/sqrt(mean_i y[t,i]^2 + norm_eps)
 //   per block of 32 consecutive i: d = max|z| / 127; q = z * (1/d) rounded to
 //   nearest with ties away from zero (d = 0 and q = 0 for an all-zero block).
-// The division and the reciprocal are IEEE fp32 operations and the rounding is
-// roundf, so q and d are a pure function of the fp32 z this kernel writes.
+// (The arithmetic of one entry and one block is in mhc_device.h, shared with
+// the pre kernels that run this epilogue in their own tail.)
 //
-// One block of 256 threads per token; each thread owns hidden quads
+// Standalone form, for the shapes whose pre kernel does not: one block of 256
+// threads per token; each thread owns hidden quads
 // q4 = tid, tid + 256, ...; the eight threads of a 32-entry block are eight
 // neighbouring lanes, so the block maximum is a three-step lane butterfly.
 #include "mhc_device.h"
@@ -34,10 +35,7 @@ __global__ __launch_bounds__(256) void zq8_kernel(const float* __restrict__ y,
   for (int k = 0; k < kZq8MaxQuads; ++k) {
     const int i = tid + 256 * k;
     v[k] = i < HQ ? yt[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    ss = fmaf(v[k].x, v[k].x, ss);
-    ss = fmaf(v[k].y, v[k].y, ss);
-    ss = fmaf(v[k].z, v[k].z, ss);
-    ss = fmaf(v[k].w, v[k].w, ss);
+    ss = sq4(v[k], ss);
   }
   // fixed-order block sum of the squares
   red[tid] = ss;
@@ -46,7 +44,7 @@ __global__ __launch_bounds__(256) void zq8_kernel(const float* __restrict__ y,
     if (tid < s) red[tid] += red[tid + s];
     __syncthreads();
   }
-  const float r = __builtin_amdgcn_rsqf(fmaf(red[0], 1.0f / (float)H, norm_eps));
+  const float r = zq8_rinv(red[0], H, norm_eps);
   const float4* w4 = reinterpret_cast<const float4*>(nw);
   float4* zt = reinterpret_cast<float4*>(z + (size_t)t * H);
   char4* qt = reinterpret_cast<char4*>(q + (size_t)t * H);
@@ -56,22 +54,12 @@ __global__ __launch_bounds__(256) void zq8_kernel(const float* __restrict__ y,
     const int i = tid + 256 * k;
     const bool in = i < HQ;  // HQ % 8 == 0: a 32-entry block is all in or all out
     const float4 w = in ? w4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 o;
-    o.x = v[k].x * r * w.x;
-    o.y = v[k].y * r * w.y;
-    o.z = v[k].z * r * w.z;
-    o.w = v[k].w * r * w.w;
-    float a = fmaxf(fmaxf(fabsf(o.x), fabsf(o.y)), fmaxf(fabsf(o.z), fabsf(o.w)));
-    // max over the eight lanes of this 32-entry block (lane bits 0-2)
-    a = fmaxf(a, dpp<0xB1>(a));   // quad_perm [1,0,3,2]
-    a = fmaxf(a, dpp<0x4E>(a));   // quad_perm [2,3,0,1]
-    a = fmaxf(a, dpp<0x141>(a));  // half-row mirror: the other quad
-    const float db = a / 127.0f;
-    const float id = db != 0.0f ? 1.0f / db : 0.0f;
+    const float4 o = zq8_norm(v[k], r, w);
+    float db;
+    const char4 c = zq8_codes(o, &db);
     if (in) {
       zt[i] = o;
-      qt[i] = make_char4((signed char)roundf(o.x * id), (signed char)roundf(o.y * id),
-                         (signed char)roundf(o.z * id), (signed char)roundf(o.w * id));
+      qt[i] = c;
       if ((tid & 7) == 0) dt[i >> 3] = db;
     }
   }
