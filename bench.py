@@ -164,6 +164,20 @@ def time_pre_zq8(mhc, torch, t, c, nw, norm_eps, out7, steps, warmup):
     def call():
         mhc.site_pre_zq8(t["x"], t["fn_w"], t["scale"], t["base"], nw, c.iters, c.eps, norm_eps,
                          out=out7)
+    return time_calls(torch, call, steps, warmup)
+
+
+def time_pre_variant(mhc, torch, t, c, out_pre, exact, steps, warmup):
+    """Mean µs of one pre call (plain or decode-exact), back to back."""
+    def call():
+        mhc.site_pre(t["x"], t["fn_w"], t["scale"], t["base"], c.iters, c.eps, out=out_pre,
+                     exact=exact)
+    return time_calls(torch, call, steps, warmup)
+
+
+def time_calls(torch, call, steps, warmup):
+    """Mean µs of call() over `steps` back-to-back calls on the current stream
+    (HIP events around each call)."""
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         call()
@@ -374,6 +388,19 @@ def main():
     epi_b = zq8_bytes(c.T, c.H)
     epi_us = zq_pre_us - pre_ms * 1e3
 
+    # ---- decode-exact batching: a 64-token verify batch and the prefill chunk
+    from mhc_inputs import make_random_shape
+    d64 = to_dev(make_random_shape(64, c.S, c.H, seed=64), torch)
+    p64, _ = alloc_out(64, c.S, c.H, torch)
+    ex = {"T64_exact_us": time_pre_variant(mhc, torch, d64, c, p64, True, args.steps, args.warmup),
+          "T64_plain_us": time_pre_variant(mhc, torch, d64, c, p64, False, args.steps,
+                                           args.warmup),
+          "T4096_exact_us": time_pre_variant(mhc, torch, t, c, out_pre, True, args.steps,
+                                             args.warmup),
+          "T4096_plain_us": round(pre_ms * 1e3, 2)}
+    ex = {k: round(v, 2) for k, v in ex.items()}
+    del d64, p64
+
     # ---- CPU oracle baseline (host cores, bounded sample)
     cpu = None if args.no_cpu_baseline else cpu_baseline(c, d)
 
@@ -414,6 +441,8 @@ def main():
             "note": "the pre call with the epilogue (z = RMS-norm(y) * nw, q8 codes and "
                     "scales); added_us = its time minus pre_us; decode sites as in decode_t1 "
                     "with the epilogue in the pre call"},
+        "pre_exact": dict(ex, note="mhc_site_pre_exact (every row bit-identical to a solo "
+                                     "T=1 call) against mhc_site_pre, same inputs, S=4 H=4096"),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

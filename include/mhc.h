@@ -107,6 +107,21 @@ int mhc_site_post(const float* x, const float* f, const float* post, const float
                   int T, int streams, int hidden, float* x_out, void* stream);
 
 /*
+ * mhc_site_pre_exact -- mhc_site_pre with decode-exact batching: every token's
+ * pre, post, comb and y are bit-identical to those of a call of mhc_site_pre on
+ * that token alone (T = 1), whatever T is and whatever else is in the batch
+ * (the hyper.rs page, doc comment of pre_exact: a batched decode row must equal
+ * the session's solo step, so the mixes of every row are reduced in the order
+ * of a solo token).  Same arguments, checks and return codes as mhc_site_pre.
+ * For T <= 16 (and T <= 2 at any S) it runs the same kernels as mhc_site_pre;
+ * above that it keeps the solo K-split instead of the faster large-batch
+ * schedules, and reads x twice.
+ */
+int mhc_site_pre_exact(const float* x, const float* fn_w, const float* scale, const float* base,
+                       int T, int streams, int hidden, int iters, float eps, float* pre,
+                       float* post, float* comb, float* y, void* stream);
+
+/*
  * mhc_site_pre_zq8 -- mhc_site_pre followed by the branch-input epilogue: the
  * RMS norm of y with weight nw and its int8 q8 encoding (the norm-and-q8 step
  * that the fused "v4z" pre kernel of the hc_fused_gate.rs page folds into the

@@ -24,8 +24,9 @@ __all__ = ["site_pre", "site_post", "site_pre_zq8", "site_pre_check", "site_post
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmhc.so")
 
-EXPORTED_SYMBOLS = ("mhc_site_pre", "mhc_site_post", "mhc_site_pre_zq8", "mhc_site_pre_check",
-                    "mhc_site_post_check", "mhc_site_pre_zq8_check", "mhc_status_string")
+EXPORTED_SYMBOLS = ("mhc_site_pre", "mhc_site_post", "mhc_site_pre_exact", "mhc_site_pre_zq8",
+                    "mhc_site_pre_check", "mhc_site_post_check", "mhc_site_pre_zq8_check",
+                    "mhc_status_string")
 
 STATUS = {0: "MHC_OK", 1: "MHC_EINVAL", 2: "MHC_EALIGN", 3: "MHC_EUNSUPPORTED",
           4: "MHC_EHIP", 5: "MHC_EOVERLAP"}
@@ -51,6 +52,8 @@ def load_library() -> ctypes.CDLL:
     vp, fl, i = ctypes.c_void_p, ctypes.c_float, ctypes.c_int
     lib.mhc_site_pre.argtypes = [vp, vp, vp, vp, i, i, i, i, fl, vp, vp, vp, vp, vp]
     lib.mhc_site_pre.restype = i
+    lib.mhc_site_pre_exact.argtypes = [vp, vp, vp, vp, i, i, i, i, fl, vp, vp, vp, vp, vp]
+    lib.mhc_site_pre_exact.restype = i
     lib.mhc_site_post.argtypes = [vp, vp, vp, vp, i, i, i, vp, vp]
     lib.mhc_site_post.restype = i
     lib.mhc_site_pre_check.argtypes = [vp, vp, vp, vp, i, i, i, i, fl, vp, vp, vp, vp]
@@ -91,9 +94,11 @@ def _stream_handle(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def site_pre(x, fn_w, scale, base, iters: int, eps: float, *, out=None, stream=None):
+def site_pre(x, fn_w, scale, base, iters: int, eps: float, *, out=None, stream=None,
+             exact: bool = False):
     """Pre half of a site.  x: [T,S,H]; fn_w: [(2+S)*S, S*H]; scale: [3]; base: [(2+S)*S].
-    Returns (pre [T,S], post [T,S], comb [T,S,S], y [T,H]); `out` may supply that tuple."""
+    Returns (pre [T,S], post [T,S], comb [T,S,S], y [T,H]); `out` may supply that tuple.
+    exact=True calls mhc_site_pre_exact (every row bit-identical to a solo T=1 call)."""
     import torch
     lib = load_library()
     if x.dim() != 3:
@@ -112,10 +117,11 @@ def site_pre(x, fn_w, scale, base, iters: int, eps: float, *, out=None, stream=N
     pre, post, comb, y = out
     ptrs = (_dev(pre, "pre", (T, S)), _dev(post, "post", (T, S)),
             _dev(comb, "comb", (T, S, S)), _dev(y, "y", (T, H)))
-    rc = lib.mhc_site_pre(px, pw, ps, pb, T, S, H, int(iters), float(eps), *ptrs,
-                          _stream_handle(stream))
+    fn, name = ((lib.mhc_site_pre_exact, "mhc_site_pre_exact") if exact
+                else (lib.mhc_site_pre, "mhc_site_pre"))
+    rc = fn(px, pw, ps, pb, T, S, H, int(iters), float(eps), *ptrs, _stream_handle(stream))
     if rc != 0:
-        raise MhcError("mhc_site_pre", rc, _status_text(lib, rc))
+        raise MhcError(name, rc, _status_text(lib, rc))
     return out
 
 

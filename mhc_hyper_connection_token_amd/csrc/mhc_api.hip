@@ -12,6 +12,7 @@ namespace {
 constexpr long kMaxElems = 1L << 31;  // T*S*H must stay below this (int indexing)
 constexpr int kMaxTokens = 1 << 23;   // bounds the flattened launch grids
 constexpr int kFusedMinTokens = 128;  // below this the split-K path fills the chip better
+constexpr int kExactChunk = 8192;     // tokens per pass of mhc_site_pre_exact
 
 int check_ptr(const void* p) {
   if (!p) return MHC_EINVAL;
@@ -241,6 +242,42 @@ int mhc_site_pre(const float* x, const float* fn_w, const float* scale, const fl
   if (rc || T == 0) return rc;
   return site_pre_run(x, fn_w, scale, base, T, streams, hidden, iters, eps, pre, post, comb, y,
                       nullptr, static_cast<hipStream_t>(stream));
+}
+
+int mhc_site_pre_exact(const float* x, const float* fn_w, const float* scale, const float* base,
+                       int T, int streams, int hidden, int iters, float eps, float* pre,
+                       float* post, float* comb, float* y, void* stream) {
+  int rc = mhc_site_pre_check(x, fn_w, scale, base, T, streams, hidden, iters, eps, pre, post,
+                              comb, y);
+  if (rc || T == 0) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // One or two tokens: the single-launch decode kernels, which define the solo result.
+  if (T <= 2)
+    return site_pre_run(x, fn_w, scale, base, T, streams, hidden, iters, eps, pre, post, comb, y,
+                        nullptr, st);
+  // Otherwise the split path with the K-split of a solo token: partials in the
+  // decode kernels' per-token order (vector ALU for S <= 4, 16-token MFMA tiles
+  // above), then the finish kernel, whose reduction order is the decode
+  // kernels' own.  Tokens go in chunks so that the partials stay bounded.
+  const int S = streams, H = hidden, n = S * H, R = (2 + S) * S;
+  const PrePlan p1 = plan_pre(1, S, H);
+  const int chunk = T < kExactChunk ? T : kExactChunk;
+  Scratch sc;
+  if ((rc = get_scratch((size_t)p1.G * chunk * (R + 1) * sizeof(float), &sc))) return rc;
+  for (int t0 = 0; t0 < T; t0 += chunk) {
+    const int tc = T - t0 < chunk ? T - t0 : chunk;
+    const float* xc = x + (size_t)t0 * n;
+    hipError_t e = S <= 4 ? mhc::launch_small_partials(xc, fn_w, tc, S, H, p1.G, p1.cpr,
+                                                       sc.general, st)
+                          : mhc::launch_partials(xc, fn_w, tc, n, R, 1, p1.G, p1.cpr, sc.general,
+                                                 st);
+    if (e == hipSuccess)
+      e = mhc::launch_finish(xc, sc.general, p1.G, tc, S, H, scale, base, iters, eps,
+                             pre + (size_t)t0 * S, post + (size_t)t0 * S,
+                             comb + (size_t)t0 * S * S, y + (size_t)t0 * H, st);
+    if (e != hipSuccess) return MHC_EHIP;
+  }
+  return MHC_OK;
 }
 
 int mhc_site_pre_zq8_check(const float* x, const float* fn_w, const float* scale,

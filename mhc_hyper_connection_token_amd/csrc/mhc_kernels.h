@@ -19,8 +19,8 @@ struct Zq8Out {
 hipError_t launch_partials(const float* x, const float* fn_w, int T, int n, int R, int ntt,
                            int G, int chunks_per_range, float* part, hipStream_t st);
 
-// Vector-ALU split-K partials for a small batch (T <= 16, S <= 4), per token in
-// the order the single-launch decode kernel uses; same part layout.
+// Vector-ALU split-K partials (S <= 4, any T in groups of 16 tokens), per token
+// in the order the single-launch decode kernel uses; same part layout.
 int small_rows_per_thread(int S);
 hipError_t launch_small_partials(const float* x, const float* fn_w, int T, int S, int H, int G,
                                  int chunks_per_range, float* part, hipStream_t st);

@@ -50,9 +50,9 @@ static hipError_t launch_partials_t(const float* x, const float* fn_w, int T, in
   return hipGetLastError();
 }
 
-// Small batches (T <= 16, S <= 4): the vector-ALU partials, one token at a time
-// in the same order as the single-launch decode kernel, so a token's result
-// does not depend on the batch it is in.
+// Vector-ALU partials (S <= 4), one token at a time in the same order as the
+// single-launch decode kernel, so a token's result does not depend on the
+// batch it is in.  Grid: (G K-ranges, groups of 16 tokens).
 template <int RPT>
 __global__ __launch_bounds__(256) void small_partials_kernel(const float* __restrict__ x,
                                                              const float* __restrict__ fn_w,
@@ -60,10 +60,11 @@ __global__ __launch_bounds__(256) void small_partials_kernel(const float* __rest
                                                              int chunks_per_range,
                                                              float* __restrict__ part) {
   const int g = blockIdx.x;
+  const int t0 = blockIdx.y * 16;
   const int k_beg = g * chunks_per_range * 16;
   const int k_end = min(n, k_beg + chunks_per_range * 16);
-  float* pg = part + (size_t)g * T * (R + 1);
-  small_partials<16, RPT>(x, fn_w, T, n, R, k_beg, k_end,
+  float* pg = part + ((size_t)g * T + t0) * (R + 1);
+  small_partials<16, RPT>(x + (size_t)t0 * n, fn_w, min(16, T - t0), n, R, k_beg, k_end,
                           [=](size_t i, float v) { pg[i] = v; });
 }
 
@@ -75,19 +76,20 @@ int small_rows_per_thread(int S) {
 
 hipError_t launch_small_partials(const float* x, const float* fn_w, int T, int S, int H, int G,
                                  int chunks_per_range, float* part, hipStream_t st) {
-  if (T < 1 || T > 16) return hipErrorInvalidValue;
+  if (T < 1 || T > 65535 * 16) return hipErrorInvalidValue;
   const int n = S * H, R = (2 + S) * S;
+  const dim3 grid(G, (T + 15) / 16);
   switch (small_rows_per_thread(S)) {
     case 1:
-      hipLaunchKernelGGL((small_partials_kernel<1>), dim3(G), dim3(256), 0, st, x, fn_w, T, n, R,
+      hipLaunchKernelGGL((small_partials_kernel<1>), grid, dim3(256), 0, st, x, fn_w, T, n, R,
                          chunks_per_range, part);
       break;
     case 2:
-      hipLaunchKernelGGL((small_partials_kernel<2>), dim3(G), dim3(256), 0, st, x, fn_w, T, n, R,
+      hipLaunchKernelGGL((small_partials_kernel<2>), grid, dim3(256), 0, st, x, fn_w, T, n, R,
                          chunks_per_range, part);
       break;
     case 4:
-      hipLaunchKernelGGL((small_partials_kernel<4>), dim3(G), dim3(256), 0, st, x, fn_w, T, n, R,
+      hipLaunchKernelGGL((small_partials_kernel<4>), grid, dim3(256), 0, st, x, fn_w, T, n, R,
                          chunks_per_range, part);
       break;
     default:
