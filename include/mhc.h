@@ -41,6 +41,8 @@
 #ifndef MHC_H
 #define MHC_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -145,6 +147,63 @@ int mhc_site_pre_zq8(const float* x, const float* fn_w, const float* scale, cons
                      const float* nw, int T, int streams, int hidden, int iters, float eps,
                      float norm_eps, float* pre, float* post, float* comb, float* y, float* z,
                      signed char* q, float* d, void* stream);
+
+/*
+ * Persistent site workspace (the hyper.rs page, doc comment of HyperDecodeWs:
+ * one set of buffers per engine, every buffer fully overwritten before it is
+ * read, the stream state ping-ponged with one spare slot, so that a decode
+ * token makes no allocation).  Here the caller provides the memory and the
+ * library never allocates on the workspace path, so a walk over sites can be
+ * captured in a HIP graph.
+ *
+ * mhc_workspace_bytes(max_tokens, streams, hidden) is the device memory a
+ * workspace needs (0 for an invalid shape; 1 <= max_tokens <= 8192).
+ * mhc_workspace_init carves `mem` (device memory, 256-byte aligned, at least
+ * that many bytes, owned by the caller and kept alive while the workspace is
+ * used) into the regions below, fills *ws (host memory of the caller) and
+ * clears the kernels' ticket with hipMemsetAsync on `stream`; it is not meant
+ * to be captured.  Returns MHC_EINVAL / MHC_EALIGN / MHC_EUNSUPPORTED /
+ * MHC_EHIP.
+ *
+ * The fields are read-only for the caller except that the current stream state
+ * state[cur] may be written (e.g. the trunk's entry state) and read at any
+ * time.  All outputs have max_tokens rows; a call with T tokens writes the
+ * first T.  z, q and d are meaningful only when hidden % 32 == 0.
+ *
+ * mhc_ws_site_pre / mhc_ws_site_pre_zq8: mhc_site_pre / mhc_site_pre_zq8 on
+ * x = state[cur] with the workspace's outputs and its own scratch (so two
+ * workspaces may run concurrently on different streams; one workspace must not).
+ * mhc_ws_site_post: mhc_site_post from state[cur] with the workspace's post and
+ * comb into state[cur ^ 1], then flips cur on the host.  A captured graph bakes
+ * the slots in: capture an even number of posts (the two sites of a layer) so
+ * that every replay starts and ends in the same slot.  0 <= T <= max_tokens; a
+ * call with T = 0 does nothing and does not flip.  Errors as the plain calls.
+ */
+typedef struct mhc_workspace {
+  int max_tokens, streams, hidden;
+  int cur;              /* index of the current stream state: 0 or 1 */
+  float* state[2];      /* [max_tokens][S][H] each */
+  float* pre;           /* [max_tokens][S] */
+  float* post;          /* [max_tokens][S] */
+  float* comb;          /* [max_tokens][S][S] */
+  float* y;             /* [max_tokens][H] */
+  float* z;             /* [max_tokens][H] */
+  signed char* q;       /* [max_tokens][H] */
+  float* d;             /* [max_tokens][ceil(H/32)] */
+  void* scratch;        /* kernel scratch: ticket header + partials / packed weight */
+  size_t scratch_bytes; /* usable scratch after the header */
+} mhc_workspace;
+
+size_t mhc_workspace_bytes(int max_tokens, int streams, int hidden);
+size_t mhc_workspace_struct_bytes(void); /* sizeof(mhc_workspace), for bindings */
+int mhc_workspace_init(mhc_workspace* ws, void* mem, size_t bytes, int max_tokens, int streams,
+                       int hidden, void* stream);
+int mhc_ws_site_pre(mhc_workspace* ws, const float* fn_w, const float* scale, const float* base,
+                    int T, int iters, float eps, void* stream);
+int mhc_ws_site_pre_zq8(mhc_workspace* ws, const float* fn_w, const float* scale,
+                        const float* base, const float* nw, int T, int iters, float eps,
+                        float norm_eps, void* stream);
+int mhc_ws_site_post(mhc_workspace* ws, const float* f, int T, void* stream);
 
 /*
  * Argument checks alone: return exactly the code mhc_site_pre / mhc_site_post

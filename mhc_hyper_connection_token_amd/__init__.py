@@ -18,14 +18,16 @@ import ctypes
 import os
 
 __all__ = ["site_pre", "site_post", "site_pre_zq8", "site_pre_check", "site_post_check",
-           "site_pre_zq8_check", "load_library", "MhcError", "LIB_PATH", "EXPORTED_SYMBOLS",
-           "STATUS"]
+           "site_pre_zq8_check", "Workspace", "workspace_bytes", "load_library", "MhcError",
+           "LIB_PATH", "EXPORTED_SYMBOLS", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmhc.so")
 
 EXPORTED_SYMBOLS = ("mhc_site_pre", "mhc_site_post", "mhc_site_pre_exact", "mhc_site_pre_zq8",
                     "mhc_site_pre_check", "mhc_site_post_check", "mhc_site_pre_zq8_check",
+                    "mhc_workspace_bytes", "mhc_workspace_struct_bytes", "mhc_workspace_init",
+                    "mhc_ws_site_pre", "mhc_ws_site_pre_zq8", "mhc_ws_site_post",
                     "mhc_status_string")
 
 STATUS = {0: "MHC_OK", 1: "MHC_EINVAL", 2: "MHC_EALIGN", 3: "MHC_EUNSUPPORTED",
@@ -68,8 +70,33 @@ def load_library() -> ctypes.CDLL:
     lib.mhc_site_pre_zq8_check.restype = i
     lib.mhc_status_string.argtypes = [i]
     lib.mhc_status_string.restype = ctypes.c_char_p
+    sz, wsp = ctypes.c_size_t, ctypes.POINTER(_WsStruct)
+    lib.mhc_workspace_bytes.argtypes = [i, i, i]
+    lib.mhc_workspace_bytes.restype = sz
+    lib.mhc_workspace_struct_bytes.argtypes = []
+    lib.mhc_workspace_struct_bytes.restype = sz
+    lib.mhc_workspace_init.argtypes = [wsp, vp, sz, i, i, i, vp]
+    lib.mhc_workspace_init.restype = i
+    lib.mhc_ws_site_pre.argtypes = [wsp, vp, vp, vp, i, i, fl, vp]
+    lib.mhc_ws_site_pre.restype = i
+    lib.mhc_ws_site_pre_zq8.argtypes = [wsp, vp, vp, vp, vp, i, i, fl, fl, vp]
+    lib.mhc_ws_site_pre_zq8.restype = i
+    lib.mhc_ws_site_post.argtypes = [wsp, vp, i, vp]
+    lib.mhc_ws_site_post.restype = i
+    if lib.mhc_workspace_struct_bytes() != ctypes.sizeof(_WsStruct):
+        raise RuntimeError("mhc_workspace layout of the library and the binding differ")
     _lib = lib
     return lib
+
+
+class _WsStruct(ctypes.Structure):
+    """Mirror of struct mhc_workspace (include/mhc.h)."""
+    _fields_ = [("max_tokens", ctypes.c_int), ("streams", ctypes.c_int),
+                ("hidden", ctypes.c_int), ("cur", ctypes.c_int),
+                ("state", ctypes.c_void_p * 2), ("pre", ctypes.c_void_p),
+                ("post", ctypes.c_void_p), ("comb", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("z", ctypes.c_void_p), ("q", ctypes.c_void_p), ("d", ctypes.c_void_p),
+                ("scratch", ctypes.c_void_p), ("scratch_bytes", ctypes.c_size_t)]
 
 
 def _status_text(lib, rc: int) -> str:
@@ -196,3 +223,102 @@ def site_pre_zq8_check(x_ptr, fn_w_ptr, scale_ptr, base_ptr, nw_ptr, T, S, H, it
     return lib.mhc_site_pre_zq8_check(x_ptr, fn_w_ptr, scale_ptr, base_ptr, nw_ptr, T, S, H,
                                       iters, float(eps), float(norm_eps), pre_ptr, post_ptr,
                                       comb_ptr, y_ptr, z_ptr, q_ptr, d_ptr)
+
+
+def workspace_bytes(max_tokens: int, streams: int, hidden: int) -> int:
+    """Device bytes a workspace of this shape needs (0 for an invalid shape)."""
+    return int(load_library().mhc_workspace_bytes(max_tokens, streams, hidden))
+
+
+class Workspace:
+    """A persistent site workspace (mhc_workspace_init and the mhc_ws_* calls).
+
+    The device memory is one torch uint8 buffer owned by this object; the library
+    carves it and never allocates on the workspace path.  Tensor views of the
+    regions: ``state`` (the current stream state, [max_tokens, S, H], writable),
+    ``pre``, ``post``, ``comb``, ``y``, ``z``, ``q``, ``d`` (max_tokens rows; a call
+    with T tokens writes the first T)."""
+
+    def __init__(self, max_tokens: int, streams: int, hidden: int, device=None, stream=None):
+        import torch
+        lib = load_library()
+        nbytes = int(lib.mhc_workspace_bytes(max_tokens, streams, hidden))
+        if nbytes == 0:
+            raise ValueError(f"invalid workspace shape ({max_tokens}, {streams}, {hidden})")
+        self._mem = torch.empty(nbytes + 256, dtype=torch.uint8,
+                                device=device if device is not None else "cuda")
+        base = self._mem.data_ptr()
+        self._base = base
+        off = (-base) % 256
+        self._ws = _WsStruct()
+        rc = lib.mhc_workspace_init(ctypes.byref(self._ws), base + off, nbytes, max_tokens,
+                                    streams, hidden, _stream_handle(stream))
+        if rc != 0:
+            raise MhcError("mhc_workspace_init", rc, _status_text(lib, rc))
+        self.max_tokens, self.streams, self.hidden = max_tokens, streams, hidden
+        T, S, H = max_tokens, streams, hidden
+        f32, i8 = torch.float32, torch.int8
+        w = self._ws
+        self._states = (self._view(w.state[0], (T, S, H), f32),
+                        self._view(w.state[1], (T, S, H), f32))
+        self.pre = self._view(w.pre, (T, S), f32)
+        self.post = self._view(w.post, (T, S), f32)
+        self.comb = self._view(w.comb, (T, S, S), f32)
+        self.y = self._view(w.y, (T, H), f32)
+        self.z = self._view(w.z, (T, H), f32)
+        self.q = self._view(w.q, (T, H), i8)
+        self.d = self._view(w.d, (T, (H + 31) // 32), f32)
+
+    def _view(self, ptr, shape, dtype):
+        import torch
+        itemsize = torch.empty((), dtype=dtype).element_size()
+        count = 1
+        for s in shape:
+            count *= s
+        o = ptr - self._base
+        return self._mem[o:o + count * itemsize].view(dtype).view(shape)
+
+    @property
+    def cur(self) -> int:
+        return int(self._ws.cur)
+
+    @property
+    def state(self):
+        """The current stream state [max_tokens, S, H] (state[cur])."""
+        return self._states[self._ws.cur]
+
+    def site_pre(self, fn_w, scale, base, iters: int, eps: float, T: int = None, stream=None):
+        lib = load_library()
+        T = self.max_tokens if T is None else T
+        S, H = self.streams, self.hidden
+        R = (2 + S) * S
+        rc = lib.mhc_ws_site_pre(ctypes.byref(self._ws), _dev(fn_w, "fn_w", (R, S * H)),
+                                 _dev(scale, "scale", (3,)), _dev(base, "base", (R,)), T,
+                                 int(iters), float(eps), _stream_handle(stream))
+        if rc != 0:
+            raise MhcError("mhc_ws_site_pre", rc, _status_text(lib, rc))
+
+    def site_pre_zq8(self, fn_w, scale, base, nw, iters: int, eps: float,
+                     norm_eps: float = 1e-5, T: int = None, stream=None):
+        lib = load_library()
+        T = self.max_tokens if T is None else T
+        S, H = self.streams, self.hidden
+        R = (2 + S) * S
+        rc = lib.mhc_ws_site_pre_zq8(ctypes.byref(self._ws), _dev(fn_w, "fn_w", (R, S * H)),
+                                     _dev(scale, "scale", (3,)), _dev(base, "base", (R,)),
+                                     _dev(nw, "nw", (H,)), T, int(iters), float(eps),
+                                     float(norm_eps), _stream_handle(stream))
+        if rc != 0:
+            raise MhcError("mhc_ws_site_pre_zq8", rc, _status_text(lib, rc))
+
+    def site_post(self, f, T: int = None, stream=None):
+        lib = load_library()
+        T = self.max_tokens if T is None else T
+        if not (f.is_cuda and f.dtype.is_floating_point and f.is_contiguous()):
+            raise ValueError("f must be a contiguous float32 GPU tensor")
+        if f.dim() != 2 or f.shape[0] < T or f.shape[1] != self.hidden:
+            raise ValueError(f"f must be [>= {T}, {self.hidden}]")
+        rc = lib.mhc_ws_site_post(ctypes.byref(self._ws), _dev(f, "f"), T,
+                                  _stream_handle(stream))
+        if rc != 0:
+            raise MhcError("mhc_ws_site_post", rc, _status_text(lib, rc))

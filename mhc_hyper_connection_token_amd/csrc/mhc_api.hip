@@ -84,6 +84,23 @@ int get_scratch(size_t bytes, Scratch* out) {
   return MHC_OK;
 }
 
+// Scratch for one call: a workspace's own area when the caller brings one (it
+// was sized for the largest request of its shape), else the library's
+// per-device area.
+struct ScratchSource {
+  const Scratch* fixed = nullptr;
+  size_t bytes = 0;
+};
+
+int acquire_scratch(const ScratchSource& src, size_t bytes, Scratch* out) {
+  if (src.fixed) {
+    if (bytes > src.bytes) return MHC_EINVAL;
+    *out = *src.fixed;
+    return MHC_OK;
+  }
+  return get_scratch(bytes, out);
+}
+
 // Split-K plan for the pre chain: token tiles of 16*ntt tokens, G K-ranges of
 // cpr 16-float chunks each.  G and the tile width depend only on (T <= 16) and
 // the shape, never on which tokens a block holds, so a token's result is the
@@ -113,6 +130,12 @@ PrePlan plan_pre(int T, int S, int H) {
   p.G = (nchunks + p.cpr - 1) / p.cpr;
   p.part_floats = (size_t)p.G * T * (R + 1);
   return p;
+}
+
+// Scratch bytes of the pre chain at T tokens (the kernel choice of site_pre_run).
+size_t pre_scratch_bytes(int T, int S, int H) {
+  if (T >= kFusedMinTokens && mhc::fused_supported(S, H)) return mhc::fused_pack_bytes(S, H);
+  return plan_pre(T, S, H).part_floats * sizeof(float);
 }
 
 }  // namespace
@@ -185,14 +208,15 @@ namespace {
 // it, otherwise as its own launch after the chain.
 int site_pre_run(const float* x, const float* fn_w, const float* scale, const float* base, int T,
                  int S, int H, int iters, float eps, float* pre, float* post, float* comb,
-                 float* y, const mhc::Zq8Out* zq, hipStream_t st) {
+                 float* y, const mhc::Zq8Out* zq, hipStream_t st,
+                 const ScratchSource& src = ScratchSource()) {
   int rc;
   const int n = S * H, R = (2 + S) * S;
   bool zq_done = false;
   if (T >= kFusedMinTokens && mhc::fused_supported(S, H)) {
     // Large batches with a slab that fits on chip: x read once.
     Scratch sc;
-    if ((rc = get_scratch(mhc::fused_pack_bytes(S, H), &sc))) return rc;
+    if ((rc = acquire_scratch(src, mhc::fused_pack_bytes(S, H), &sc))) return rc;
     if (mhc::launch_fused_pre(x, fn_w, scale, base, T, S, H, iters, eps, pre, post, comb, y,
                               sc.general, zq, st) != hipSuccess)
       return MHC_EHIP;
@@ -200,7 +224,7 @@ int site_pre_run(const float* x, const float* fn_w, const float* scale, const fl
   } else {
     const PrePlan p = plan_pre(T, S, H);
     Scratch sc;
-    if ((rc = get_scratch(p.part_floats * sizeof(float), &sc))) return rc;
+    if ((rc = acquire_scratch(src, p.part_floats * sizeof(float), &sc))) return rc;
     float* part = sc.general;
     hipError_t e;
     if (T <= 2) {
@@ -335,6 +359,149 @@ int mhc_site_post(const float* x, const float* f, const float* post, const float
   if (mhc::launch_post(x, f, post, comb, T, streams, hidden, x_out,
                        static_cast<hipStream_t>(stream)) != hipSuccess)
     return MHC_EHIP;
+  return MHC_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- workspace
+// Caller memory carved into 256-byte aligned regions, in this order: the kernel
+// scratch (ticket header + the largest partials / packed weight of any
+// T <= max_tokens), the two stream states, pre, post, comb, y, z, q, d.
+namespace {
+constexpr size_t kWsAlign = 256;
+size_t ws_round(size_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+struct WsLayout {
+  size_t scratch_general, off[10], total;
+};
+
+bool ws_layout(int max_tokens, int S, int H, WsLayout* L) {
+  if (max_tokens < 1 || max_tokens > kExactChunk || check_shape(max_tokens, S, H) != MHC_OK)
+    return false;
+  size_t general = 0;
+  for (int t = 1; t <= max_tokens; ++t) {
+    const size_t b = pre_scratch_bytes(t, S, H);
+    if (b > general) general = b;
+  }
+  const size_t T = max_tokens;
+  const size_t sizes[10] = {kScratchHeader + general, T * S * H * 4, T * S * H * 4, T * S * 4,
+                            T * S * 4, T * S * S * 4, T * H * 4, T * H * 4, T * H,
+                            T * ((H + 31) / 32) * 4};
+  size_t o = 0;
+  for (int i = 0; i < 10; ++i) {
+    L->off[i] = o;
+    o += ws_round(sizes[i]);
+  }
+  L->scratch_general = general;
+  L->total = o;
+  return true;
+}
+
+int ws_ok(const mhc_workspace* ws, int T) {
+  if (!ws || !ws->scratch || (ws->cur != 0 && ws->cur != 1)) return MHC_EINVAL;
+  if (T < 0 || T > ws->max_tokens) return MHC_EINVAL;
+  return MHC_OK;
+}
+
+ScratchSource ws_scratch(const mhc_workspace* ws, Scratch* holder) {
+  char* b = static_cast<char*>(ws->scratch);
+  holder->counter = reinterpret_cast<unsigned int*>(b);
+  holder->general = reinterpret_cast<float*>(b + kScratchHeader);
+  ScratchSource src;
+  src.fixed = holder;
+  src.bytes = ws->scratch_bytes;
+  return src;
+}
+}  // namespace
+
+extern "C" {
+
+size_t mhc_workspace_bytes(int max_tokens, int streams, int hidden) {
+  WsLayout L;
+  return ws_layout(max_tokens, streams, hidden, &L) ? L.total : 0;
+}
+
+size_t mhc_workspace_struct_bytes(void) { return sizeof(mhc_workspace); }
+
+int mhc_workspace_init(mhc_workspace* ws, void* mem, size_t bytes, int max_tokens, int streams,
+                       int hidden, void* stream) {
+  if (!ws || !mem) return MHC_EINVAL;
+  WsLayout L;
+  if (!ws_layout(max_tokens, streams, hidden, &L)) {
+    const int rc = check_shape(max_tokens, streams, hidden);
+    return rc ? rc : MHC_EINVAL;
+  }
+  if (reinterpret_cast<uintptr_t>(mem) % kWsAlign != 0) return MHC_EALIGN;
+  if (bytes < L.total) return MHC_EINVAL;
+  char* b = static_cast<char*>(mem);
+  ws->max_tokens = max_tokens;
+  ws->streams = streams;
+  ws->hidden = hidden;
+  ws->cur = 0;
+  ws->scratch = b + L.off[0];
+  ws->scratch_bytes = L.scratch_general;
+  ws->state[0] = reinterpret_cast<float*>(b + L.off[1]);
+  ws->state[1] = reinterpret_cast<float*>(b + L.off[2]);
+  ws->pre = reinterpret_cast<float*>(b + L.off[3]);
+  ws->post = reinterpret_cast<float*>(b + L.off[4]);
+  ws->comb = reinterpret_cast<float*>(b + L.off[5]);
+  ws->y = reinterpret_cast<float*>(b + L.off[6]);
+  ws->z = reinterpret_cast<float*>(b + L.off[7]);
+  ws->q = reinterpret_cast<signed char*>(b + L.off[8]);
+  ws->d = reinterpret_cast<float*>(b + L.off[9]);
+  // the decode ticket starts at zero; the kernels leave it there
+  if (hipMemsetAsync(ws->scratch, 0, kScratchHeader, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return MHC_EHIP;
+  return MHC_OK;
+}
+
+int mhc_ws_site_pre(mhc_workspace* ws, const float* fn_w, const float* scale, const float* base,
+                    int T, int iters, float eps, void* stream) {
+  int rc = ws_ok(ws, T);
+  if (rc) return rc;
+  const float* x = ws->state[ws->cur];
+  if ((rc = mhc_site_pre_check(x, fn_w, scale, base, T, ws->streams, ws->hidden, iters, eps,
+                               ws->pre, ws->post, ws->comb, ws->y)) ||
+      T == 0)
+    return rc;
+  Scratch holder;
+  return site_pre_run(x, fn_w, scale, base, T, ws->streams, ws->hidden, iters, eps, ws->pre,
+                      ws->post, ws->comb, ws->y, nullptr, static_cast<hipStream_t>(stream),
+                      ws_scratch(ws, &holder));
+}
+
+int mhc_ws_site_pre_zq8(mhc_workspace* ws, const float* fn_w, const float* scale,
+                        const float* base, const float* nw, int T, int iters, float eps,
+                        float norm_eps, void* stream) {
+  int rc = ws_ok(ws, T);
+  if (rc) return rc;
+  const float* x = ws->state[ws->cur];
+  if ((rc = mhc_site_pre_zq8_check(x, fn_w, scale, base, nw, T, ws->streams, ws->hidden, iters,
+                                   eps, norm_eps, ws->pre, ws->post, ws->comb, ws->y, ws->z,
+                                   ws->q, ws->d)) ||
+      T == 0)
+    return rc;
+  const mhc::Zq8Out zq{nw, norm_eps, ws->z, ws->q, ws->d};
+  Scratch holder;
+  return site_pre_run(x, fn_w, scale, base, T, ws->streams, ws->hidden, iters, eps, ws->pre,
+                      ws->post, ws->comb, ws->y, &zq, static_cast<hipStream_t>(stream),
+                      ws_scratch(ws, &holder));
+}
+
+int mhc_ws_site_post(mhc_workspace* ws, const float* f, int T, void* stream) {
+  int rc = ws_ok(ws, T);
+  if (rc) return rc;
+  const float* x = ws->state[ws->cur];
+  float* x_out = ws->state[ws->cur ^ 1];
+  if ((rc = mhc_site_post_check(x, f, ws->post, ws->comb, T, ws->streams, ws->hidden, x_out)) ||
+      T == 0)
+    return rc;  // nothing written: the state stays where it is
+  if (mhc::launch_post(x, f, ws->post, ws->comb, T, ws->streams, ws->hidden, x_out,
+                       static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MHC_EHIP;
+  ws->cur ^= 1;
   return MHC_OK;
 }
 

@@ -52,20 +52,47 @@ static hipError_t launch_partials_t(const float* x, const float* fn_w, int T, in
 
 // Vector-ALU partials (S <= 4), one token at a time in the same order as the
 // single-launch decode kernel, so a token's result does not depend on the
-// batch it is in.  Grid: (G K-ranges, groups of 16 tokens).
-template <int RPT>
+// batch it is in.  Grid: (G K-ranges, Y); block (g, y) takes the groups of
+// kSmallGroup tokens y, y + Y, ..., with the weight quads of its K-range held
+// in registers and the next group's x requested while the current one is
+// reduced.  QL = column quads per lane (a K-range of at most 128*QL floats).
+constexpr int kSmallGroup = 4;
+constexpr int kSmallBlocks = 2048;  // target grid size at large T
+
+template <int RPT, int QL>
 __global__ __launch_bounds__(256) void small_partials_kernel(const float* __restrict__ x,
                                                              const float* __restrict__ fn_w,
                                                              int T, int n, int R,
                                                              int chunks_per_range,
                                                              float* __restrict__ part) {
   const int g = blockIdx.x;
-  const int t0 = blockIdx.y * 16;
   const int k_beg = g * chunks_per_range * 16;
   const int k_end = min(n, k_beg + chunks_per_range * 16);
-  float* pg = part + ((size_t)g * T + t0) * (R + 1);
-  small_partials<16, RPT>(x + (size_t)t0 * n, fn_w, min(16, T - t0), n, R, k_beg, k_end,
-                          [=](size_t i, float v) { pg[i] = v; });
+  float* pg = part + (size_t)g * T * (R + 1);
+  small_partials_groups<kSmallGroup, RPT, QL>(
+      x, fn_w, T, n, R, k_beg, k_end, blockIdx.y, gridDim.y,
+      [=](int t, int r, float v) { pg[(size_t)t * (R + 1) + r] = v; });
+}
+
+// The same partials for K-ranges longer than 512 floats: the plain per-group
+// loop of small_partials, without holding the weight quads.
+template <int RPT>
+__global__ __launch_bounds__(256) void small_partials_long_kernel(const float* __restrict__ x,
+                                                                  const float* __restrict__ fn_w,
+                                                                  int T, int n, int R,
+                                                                  int chunks_per_range,
+                                                                  float* __restrict__ part) {
+  const int g = blockIdx.x;
+  const int groups = (T + kSmallGroup - 1) / kSmallGroup;
+  const int k_beg = g * chunks_per_range * 16;
+  const int k_end = min(n, k_beg + chunks_per_range * 16);
+  float* pg = part + (size_t)g * T * (R + 1);
+  for (int tg = blockIdx.y; tg < groups; tg += gridDim.y) {
+    const int t0 = tg * kSmallGroup;
+    float* pt = pg + (size_t)t0 * (R + 1);
+    small_partials<kSmallGroup, RPT>(x + (size_t)t0 * n, fn_w, min(kSmallGroup, T - t0), n, R,
+                                     k_beg, k_end, [=](size_t i, float v) { pt[i] = v; });
+  }
 }
 
 int small_rows_per_thread(int S) {
@@ -76,26 +103,32 @@ int small_rows_per_thread(int S) {
 
 hipError_t launch_small_partials(const float* x, const float* fn_w, int T, int S, int H, int G,
                                  int chunks_per_range, float* part, hipStream_t st) {
-  if (T < 1 || T > 65535 * 16) return hipErrorInvalidValue;
+  if (T < 1 || G < 1) return hipErrorInvalidValue;
   const int n = S * H, R = (2 + S) * S;
-  const dim3 grid(G, (T + 15) / 16);
-  switch (small_rows_per_thread(S)) {
-    case 1:
-      hipLaunchKernelGGL((small_partials_kernel<1>), grid, dim3(256), 0, st, x, fn_w, T, n, R,
-                         chunks_per_range, part);
-      break;
-    case 2:
-      hipLaunchKernelGGL((small_partials_kernel<2>), grid, dim3(256), 0, st, x, fn_w, T, n, R,
-                         chunks_per_range, part);
-      break;
-    case 4:
-      hipLaunchKernelGGL((small_partials_kernel<4>), grid, dim3(256), 0, st, x, fn_w, T, n, R,
-                         chunks_per_range, part);
-      break;
-    default:
-      return hipErrorInvalidValue;
+  const int groups = (T + kSmallGroup - 1) / kSmallGroup;
+  const int ymax = kSmallBlocks / G > 1 ? kSmallBlocks / G : 1;
+  const dim3 grid(G, groups < ymax ? groups : ymax);
+  const int ql = (chunks_per_range * 4 + 31) / 32;  // column quads per lane
+  const int rpt = small_rows_per_thread(S);
+#define MHC_SP(RP_, QL_)                                                                       \
+  if (rpt == RP_ && ql <= QL_) {                                                               \
+    hipLaunchKernelGGL((small_partials_kernel<RP_, QL_>), grid, dim3(256), 0, st, x, fn_w, T, n, \
+                       R, chunks_per_range, part);                                             \
+    return hipGetLastError();                                                                  \
   }
-  return hipGetLastError();
+  MHC_SP(1, 1) MHC_SP(1, 2) MHC_SP(1, 4)
+  MHC_SP(2, 1) MHC_SP(2, 2) MHC_SP(2, 4)
+  MHC_SP(4, 1) MHC_SP(4, 2) MHC_SP(4, 4)
+#undef MHC_SP
+#define MHC_SL(RP_)                                                                            \
+  if (rpt == RP_) {                                                                            \
+    hipLaunchKernelGGL((small_partials_long_kernel<RP_>), grid, dim3(256), 0, st, x, fn_w, T,   \
+                       n, R, chunks_per_range, part);                                          \
+    return hipGetLastError();                                                                  \
+  }
+  MHC_SL(1) MHC_SL(2) MHC_SL(4)
+#undef MHC_SL
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_partials(const float* x, const float* fn_w, int T, int n, int R, int ntt,

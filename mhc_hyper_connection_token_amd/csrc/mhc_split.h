@@ -176,15 +176,137 @@ __device__ __forceinline__ void block_partials(const float* __restrict__ x,
   }
 }
 
+// ---------------------------------------------------------------- 32-lane tree sums
+// The value of the lane whose index (within its 32-lane half) differs in bit B.
+template <int B>
+__device__ __forceinline__ float lane_xor(float v) {
+  static_assert(B >= 0 && B <= 3, "bit 4 goes through permlane16_swap");
+  if constexpr (B == 0) return dpp<0xB1>(v);  // quad_perm [1,0,3,2]
+  if constexpr (B == 1) return dpp<0x4E>(v);  // quad_perm [2,3,0,1]
+  if constexpr (B == 2)                       // ds_swizzle, bit mode: xor mask 4
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F));
+  return dpp<0x128>(v);  // row_ror:8 == lane ^ 8 within a row of 16
+}
+
+// One level of tree32: the pairs of lanes that differ in bit B add their values.
+// With NV >= 2 values left the level is transposed: each lane hands half of its
+// values to the partner, the lane with bit B clear keeping the lower half of the
+// index range and its partner the upper half, so every add does useful work.
+template <int B, int NV>
+__device__ __forceinline__ void tree32_level(float* v, int lane) {
+  if constexpr (NV >= 2) {
+    constexpr int H = NV / 2;
+    if constexpr (B == 4) {
+#pragma unroll
+      for (int j = 0; j < H; ++j) {
+        // swaps row 1 of v[j] with row 0 of v[j + H]: both rows then hold
+        // (row 0 value) and (row 1 value) of their own index
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[j]), __float_as_uint(v[j + H]),
+                                                  false, false);
+        v[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      }
+    } else {
+      const bool hi = (lane >> B) & 1;
+#pragma unroll
+      for (int j = 0; j < H; ++j) {
+        const float send = hi ? v[j] : v[j + H];
+        const float keep = hi ? v[j + H] : v[j];
+        v[j] = keep + lane_xor<B>(send);
+      }
+    }
+  } else {
+    if constexpr (B == 4)
+      v[0] = swap16_sum(v[0]);
+    else
+      v[0] = v[0] + lane_xor<B>(v[0]);
+  }
+}
+
+// Sums over the 32 lanes of each half-wave of V (a power of two) values per
+// lane.  Every sum is the balanced binary tree over lanes 0..31 in lane order
+// (pairs differing in bit 0 first, then bit 1, ..., bit 4), exactly the tree of
+// a plain five-step butterfly on one value, so the bits do not depend on V or on
+// where the value sits.  On return the lane holds max(V/32, 1) sums in v[0..):
+// sum j of lane l is original index tree32_index<V>(l, j); with V < 32 the lanes
+// that differ only in bits log2(V) and up hold the same sums.
+template <int V>
+__device__ __forceinline__ void tree32(float (&v)[V], int lane) {
+  tree32_level<0, V>(v, lane);
+  tree32_level<1, (V >= 2 ? V / 2 : 1)>(v, lane);
+  tree32_level<2, (V >= 4 ? V / 4 : 1)>(v, lane);
+  tree32_level<3, (V >= 8 ? V / 8 : 1)>(v, lane);
+  tree32_level<4, (V >= 16 ? V / 16 : 1)>(v, lane);
+}
+template <int V>
+__device__ __forceinline__ constexpr int tree32_log2() {
+  return V <= 1 ? 0 : 1 + tree32_log2<V / 2>();
+}
+template <int V>
+__device__ __forceinline__ int tree32_index(int lane, int j) {
+  constexpr int m = tree32_log2<V>();
+  constexpr int lv = m < 5 ? m : 5;  // transposed levels
+  int o = 0;
+#pragma unroll
+  for (int b = 0; b < lv; ++b) o |= ((lane >> b) & 1) << (m - 1 - b);
+  return o + j;
+}
+
 // Split-K partials of a small batch (T <= TMAX tokens) on the vector ALU: for
 // every token t and row r < R the dot of fn_w[r, k_beg:k_end] with
 // x[t, k_beg:k_end], and at r == R the sum of squares of that slice, handed to
 // sink(t*(R+1) + r, value).  256 threads = 8 row slots x 32 lanes: lane l of
 // slot s takes the column quads l, l + 32, ... and rows s, s + 8, s + 16, ...
 // (RPT of them), so every weight load is a coalesced run of one row.  A
-// token's arithmetic (the order of its products and of the 32-lane butterfly
-// sum) does not depend on T or TMAX: a token's partials are the same in any
-// small batch.  k_beg and k_end are multiples of 4.
+// token's arithmetic (the order of its products and the 32-lane tree of tree32)
+// does not depend on T or TMAX: a token's partials are the same in any small
+// batch.  k_beg and k_end are multiples of 4.
+// One column quad of small_partials: acc[i][t] += fn_w[r_i, quad] . x[t, quad]
+// (row R: x . x), four fused multiply-adds in element order.
+template <int TMAX, int RPT>
+__device__ __forceinline__ void small_quad(float (&acc)[RPT][TMAX], const float4 (&w)[RPT],
+                                           const float4 (&xv)[TMAX], int slot, int R) {
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = slot + 8 * i;
+    const float4 wi = r == R ? make_float4(1.f, 1.f, 1.f, 1.f) : w[i];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      // the sum-of-squares row multiplies x by itself
+      const float4 a = r == R ? xv[t] : wi;
+      float v = acc[i][t];
+      v = fmaf(a.x, xv[t].x, v);
+      v = fmaf(a.y, xv[t].y, v);
+      v = fmaf(a.z, xv[t].z, v);
+      v = fmaf(a.w, xv[t].w, v);
+      acc[i][t] = v;
+    }
+  }
+}
+
+// The 32-lane tree of every (row, token) lane partial, handed to sink(t*(R+1) + r).
+template <int TMAX, int RPT, class Sink>
+__device__ __forceinline__ void small_tree_out(float (&acc)[RPT][TMAX], int l, int slot, int T,
+                                               int R, Sink sink) {
+  const int RP = R + 1;
+  constexpr int V = RPT * TMAX;
+  float v[V];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) v[i * TMAX + t] = acc[i][t];
+  tree32<V>(v, l);
+  constexpr int m = tree32_log2<V>();
+  if (m >= 5 || (l >> m) == 0) {
+#pragma unroll
+    for (int j = 0; j < (V >= 32 ? V / 32 : 1); ++j) {
+      const int o = tree32_index<V>(l, j);
+      const int i = o / TMAX, t = o % TMAX;
+      const int r = slot + 8 * i;
+      if (t < T && r <= R) sink((size_t)t * RP + r, v[j]);
+    }
+  }
+}
+
 template <int TMAX, int RPT, class Sink>
 __device__ __forceinline__ void small_partials(const float* __restrict__ x,
                                                const float* __restrict__ fn_w, int T, int n,
@@ -209,36 +331,72 @@ __device__ __forceinline__ void small_partials(const float* __restrict__ x,
 #pragma unroll
     for (int t = 0; t < TMAX; ++t)
       xv[t] = *reinterpret_cast<const float4*>(x + (size_t)(t < T ? t : 0) * n + col);
+    small_quad<TMAX, RPT>(acc, w, xv, slot, R);
+  }
+  small_tree_out<TMAX, RPT>(acc, l, slot, T, R, sink);
+}
+
+// small_partials over many groups of TMAX tokens of one K-range (at most 32*QL
+// column quads): the weight quads are loaded once, and each group's x quads are
+// requested while the previous group is being reduced.  Group tg covers tokens
+// [tg*TMAX, tg*TMAX + TMAX); this thread takes groups tg0, tg0 + step, ...
+// Every token gets exactly the arithmetic of small_partials.  sink(t, r, v)
+// receives the partial of token t (global index) and row r <= R.
+template <int TMAX, int RPT, int QL, class Sink>
+__device__ __forceinline__ void small_partials_groups(const float* __restrict__ x,
+                                                      const float* __restrict__ fn_w, int T,
+                                                      int n, int R, int k_beg, int k_end,
+                                                      int tg0, int step, Sink sink) {
+  const int tid = threadIdx.x;
+  const int l = tid & 31, slot = tid >> 5;
+  const int nq = (k_end - k_beg) >> 2;
+  const int groups = (T + TMAX - 1) / TMAX;
+  if (tg0 >= groups) return;
+  float4 w[QL][RPT];
+#pragma unroll
+  for (int u = 0; u < QL; ++u) {
+    const int q = l + 32 * u;
+    const int col = k_beg + 4 * (q < nq ? q : 0);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int r = slot + 8 * i;
-      const float4 wi = r == R ? make_float4(1.f, 1.f, 1.f, 1.f) : w[i];
-#pragma unroll
-      for (int t = 0; t < TMAX; ++t) {
-        // the sum-of-squares row multiplies x by itself
-        const float4 a = r == R ? xv[t] : wi;
-        float v = acc[i][t];
-        v = fmaf(a.x, xv[t].x, v);
-        v = fmaf(a.y, xv[t].y, v);
-        v = fmaf(a.z, xv[t].z, v);
-        v = fmaf(a.w, xv[t].w, v);
-        acc[i][t] = v;
-      }
+      w[u][i] = *reinterpret_cast<const float4*>(fn_w + (size_t)(r < R ? r : 0) * n + col);
     }
   }
-  const int RP = R + 1;
+  auto load_x = [&](int tg, float4 (&xv)[QL][TMAX]) {
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int r = slot + 8 * i;
+    for (int u = 0; u < QL; ++u) {
+      const int q = l + 32 * u;
+      const int col = k_beg + 4 * (q < nq ? q : 0);
 #pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-      float v = acc[i][t];
-      v = sum_xor1_2(v);
-      v = sum_xor4_in8(v);
-      v = sum_xor8_in16(v);
-      v = swap16_sum(v);
-      if (l == 0 && t < T && r <= R) sink((size_t)t * RP + r, v);
+      for (int t = 0; t < TMAX; ++t) {
+        const int tok = tg * TMAX + t;
+        xv[u][t] = *reinterpret_cast<const float4*>(x + (size_t)(tok < T ? tok : 0) * n + col);
+      }
     }
+  };
+  float4 xa[QL][TMAX], xb[QL][TMAX];
+  load_x(tg0, xa);
+  for (int tg = tg0; tg < groups; tg += step) {
+    const bool more = tg + step < groups;  // the same in every thread
+    if (more) load_x(tg + step, xb);
+    float acc[RPT][TMAX];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t) acc[i][t] = 0.f;
+#pragma unroll
+    for (int u = 0; u < QL; ++u)
+      if (l + 32 * u < nq) small_quad<TMAX, RPT>(acc, w[u], xa[u], slot, R);
+    const int t0 = tg * TMAX;
+    small_tree_out<TMAX, RPT>(acc, l, slot, min(TMAX, T - t0), R, [&](size_t i, float v) {
+      const int RP = R + 1;
+      sink(t0 + (int)(i / RP), (int)(i % RP), v);
+    });
+#pragma unroll
+    for (int u = 0; u < QL; ++u)
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t) xa[u][t] = xb[u][t];
   }
 }
 

@@ -158,3 +158,64 @@ def test_zq8_check(lib):
     # the pre-site checks still apply
     assert mhc.site_pre_zq8_check(x, w, sc, b, nw, T, S, H, 0, 1e-6, 1e-5, pre, post, comb, y, z,
                                   q, d) == EINVAL
+
+
+# ------------------------------------------------------------------ workspace (host side)
+def test_workspace_bytes_cover_every_region(lib):
+    for T, S, H in [(1, 4, 4096), (2, 8, 7168), (64, 4, 4096), (130, 4, 4096), (8192, 1, 32)]:
+        b = mhc.workspace_bytes(T, S, H)
+        R = (2 + S) * S
+        regions = (2 * T * S * H * 4 + 2 * T * S * 4 + T * S * S * 4 + 2 * T * H * 4 + T * H
+                   + T * ((H + 31) // 32) * 4)
+        assert b % 256 == 0
+        # the regions plus the ticket header and at least one token's partials
+        assert b >= regions + 256 + (R + 1) * 4
+        assert mhc.workspace_bytes(T + 1, S, H) >= b if T < 8192 else True
+
+
+def test_workspace_bytes_refuses_bad_shapes(lib):
+    for args in [(0, 4, 4096), (8193, 4, 4096), (1, 9, 4096), (1, 0, 4096), (1, 4, 4098),
+                 (1, 4, 0), (-1, 4, 4096)]:
+        assert mhc.workspace_bytes(*args) == 0, args
+
+
+def test_workspace_struct_matches_binding(lib):
+    assert lib.mhc_workspace_struct_bytes() == ctypes.sizeof(mhc._WsStruct)
+
+
+def test_workspace_init_refuses_before_any_gpu_work(lib):
+    ws = mhc._WsStruct()
+    need = mhc.workspace_bytes(4, 4, 4096)
+    assert lib.mhc_workspace_init(None, 1 << 30, need, 4, 4, 4096, None) == EINVAL
+    assert lib.mhc_workspace_init(ctypes.byref(ws), None, need, 4, 4, 4096, None) == EINVAL
+    assert lib.mhc_workspace_init(ctypes.byref(ws), (1 << 30) + 16, need, 4, 4, 4096,
+                                  None) == EALIGN
+    assert lib.mhc_workspace_init(ctypes.byref(ws), 1 << 30, need - 256, 4, 4, 4096,
+                                  None) == EINVAL
+    assert lib.mhc_workspace_init(ctypes.byref(ws), 1 << 30, need, 4, 9, 4096, None) == EUNSUP
+    assert lib.mhc_workspace_init(ctypes.byref(ws), 1 << 30, need, 0, 4, 4096, None) == EINVAL
+
+
+def test_ws_calls_refuse_before_any_gpu_work(lib):
+    ws = mhc._WsStruct()  # never initialised: no scratch
+    assert lib.mhc_ws_site_pre(ctypes.byref(ws), 1 << 30, 1 << 31, 1 << 32, 1, 20, 1e-6,
+                               None) == EINVAL
+    assert lib.mhc_ws_site_post(None, 1 << 30, 1, None) == EINVAL
+    # a laid-out workspace (fake addresses): tokens past max_tokens, bad iterations, eps
+    ws.max_tokens, ws.streams, ws.hidden, ws.cur = 4, 4, 4096, 0
+    base = 1 << 34
+    for i, name in enumerate(("pre", "post", "comb", "y", "z", "q", "d", "scratch")):
+        setattr(ws, name, base + (i + 2) * (1 << 24))
+    ws.state[0], ws.state[1] = base, base + (1 << 24)
+    ws.scratch_bytes = 1 << 20
+    w, s, b = 1 << 36, (1 << 36) + (1 << 24), (1 << 36) + (1 << 25)
+    assert lib.mhc_ws_site_pre(ctypes.byref(ws), w, s, b, 5, 20, 1e-6, None) == EINVAL
+    assert lib.mhc_ws_site_pre(ctypes.byref(ws), w, s, b, 4, 0, 1e-6, None) == EINVAL
+    assert lib.mhc_ws_site_pre(ctypes.byref(ws), w, s, b, 4, 20, 0.0, None) == EINVAL
+    assert lib.mhc_ws_site_pre(ctypes.byref(ws), None, s, b, 4, 20, 1e-6, None) == EINVAL
+    # the stream-state slot index must be 0 or 1
+    ws.cur = 2
+    assert lib.mhc_ws_site_post(ctypes.byref(ws), w, 1, None) == EINVAL
+    ws.cur = 0
+    # T = 0 is a no-op that leaves the state slot alone
+    assert lib.mhc_ws_site_post(ctypes.byref(ws), w, 0, None) == OK and ws.cur == 0

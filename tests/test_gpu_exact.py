@@ -5,7 +5,8 @@ page, doc comment of pre_exact), and within the oracle's tolerances.
 Shapes cover the solo decode kernels (T <= 2), the small-batch split (T <= 16),
 the sizes where mhc_site_pre would switch to the token-tiled MFMA and fused
 schedules (17 <= T, T >= 128), S above 4 (16-token MFMA partials), and more
-tokens than one pass of the exact path holds (8192)."""
+tokens than one pass of the exact path holds (8192).  The K-range per block runs
+from 128 floats (one column quad per lane) to 2048 (the long-range kernel)."""
 import numpy as np
 import pytest
 
@@ -59,7 +60,8 @@ def _check(mhc, d, iters, eps, rows, label):
 @pytest.mark.parametrize("T,S,H", [(1, 4, 4096), (2, 4, 4096), (2, 8, 1024), (3, 4, 4096),
                                    (16, 3, 512), (17, 4, 4096), (40, 8, 1024),
                                    (130, 4, 4096), (129, 6, 512), (300, 2, 1056),
-                                   (257, 1, 64)])
+                                   (257, 1, 64), (5, 4, 16384), (3, 2, 65536),
+                                   (40, 1, 65536)])
 def test_exact_rows_equal_solo(mhc, T, S, H):
     d = make_random_shape(T, S, H, seed=3 * T + S)
     rows = sorted({0, 1 % T, T // 2, T - 1})
