@@ -115,8 +115,9 @@ int mhc_site_post(const float* x, const float* f, const float* post, const float
  * (the hyper.rs page, doc comment of pre_exact: a batched decode row must equal
  * the session's solo step, so the mixes of every row are reduced in the order
  * of a solo token).  Same arguments, checks and return codes as mhc_site_pre.
- * For T <= 16 (and T <= 2 at any S) it runs the same kernels as mhc_site_pre;
- * above that it keeps the solo K-split instead of the faster large-batch
+ * mhc_site_pre itself already has this property for T < 256 when S <= 4 and
+ * for T <= 64 when S > 4 (there the two calls run the same kernels); above
+ * that this call keeps the solo K-split instead of the faster large-batch
  * schedules, and reads x twice.
  */
 int mhc_site_pre_exact(const float* x, const float* fn_w, const float* scale, const float* base,

@@ -11,7 +11,8 @@ namespace {
 
 constexpr long kMaxElems = 1L << 31;  // T*S*H must stay below this (int indexing)
 constexpr int kMaxTokens = 1 << 23;   // bounds the flattened launch grids
-constexpr int kFusedMinTokens = 128;  // below this the split-K path fills the chip better
+constexpr int kFusedMinTokens = 256;  // below this the split-K path fills the chip better
+constexpr int kSoloPlanMaxWide = 64;  // S > 4: up to this T the solo K-split with 16-token tiles
 constexpr int kExactChunk = 8192;     // tokens per pass of mhc_site_pre_exact
 
 int check_ptr(const void* p) {
@@ -110,6 +111,20 @@ struct PrePlan {
   size_t part_floats;
 };
 
+PrePlan plan_pre(int T, int S, int H);
+
+// The plan the pre chain uses at T tokens on the split path.  Where the solo
+// token's K-split is also the faster schedule (S <= 4 below the fused kernel's
+// threshold, S > 4 up to 64 tokens) it is kept, which makes those rows
+// bit-identical to solo calls; larger batches take wider ranges and tiles.
+PrePlan plan_split(int T, int S, int H) {
+  const bool solo = S <= 4 ? T < kFusedMinTokens : T <= kSoloPlanMaxWide;
+  if (!solo) return plan_pre(T, S, H);
+  PrePlan p = plan_pre(1, S, H);
+  p.part_floats = (size_t)p.G * T * ((2 + S) * S + 1);
+  return p;
+}
+
 PrePlan plan_pre(int T, int S, int H) {
   const int n = S * H, R = (2 + S) * S, nrt = (R + 15) / 16;
   const int nchunks = (n + 15) / 16;
@@ -135,7 +150,7 @@ PrePlan plan_pre(int T, int S, int H) {
 // Scratch bytes of the pre chain at T tokens (the kernel choice of site_pre_run).
 size_t pre_scratch_bytes(int T, int S, int H) {
   if (T >= kFusedMinTokens && mhc::fused_supported(S, H)) return mhc::fused_pack_bytes(S, H);
-  return plan_pre(T, S, H).part_floats * sizeof(float);
+  return plan_split(T, S, H).part_floats * sizeof(float);
 }
 
 }  // namespace
@@ -222,7 +237,7 @@ int site_pre_run(const float* x, const float* fn_w, const float* scale, const fl
       return MHC_EHIP;
     zq_done = true;
   } else {
-    const PrePlan p = plan_pre(T, S, H);
+    const PrePlan p = plan_split(T, S, H);
     Scratch sc;
     if ((rc = acquire_scratch(src, p.part_floats * sizeof(float), &sc))) return rc;
     float* part = sc.general;
@@ -239,7 +254,8 @@ int site_pre_run(const float* x, const float* fn_w, const float* scale, const fl
                                    sc.counter, pre, post, comb, y, st);
       }
     } else {
-      e = (T <= 16 && S <= 4)
+      // S <= 4 below the fused threshold: the decode kernels' vector-ALU partials
+      e = (S <= 4 && T < kFusedMinTokens)
               ? mhc::launch_small_partials(x, fn_w, T, S, H, p.G, p.cpr, part, st)
               : mhc::launch_partials(x, fn_w, T, n, R, p.ntt, p.G, p.cpr, part, st);
       if (e == hipSuccess)

@@ -3,8 +3,8 @@ bit-identical to a solo T=1 call of mhc_site_pre on that token (the hyper.rs
 page, doc comment of pre_exact), and within the oracle's tolerances.
 
 Shapes cover the solo decode kernels (T <= 2), the small-batch split (T <= 16),
-the sizes where mhc_site_pre would switch to the token-tiled MFMA and fused
-schedules (17 <= T, T >= 128), S above 4 (16-token MFMA partials), and more
+the sizes where mhc_site_pre switches to its large-batch schedules (the fused
+kernel from 256 tokens at S <= 4, wider MFMA tiles above 64 at S > 4), and more
 tokens than one pass of the exact path holds (8192).  The K-range per block runs
 from 128 floats (one column quad per lane) to 2048 (the long-range kernel)."""
 import numpy as np
@@ -60,6 +60,7 @@ def _check(mhc, d, iters, eps, rows, label):
 @pytest.mark.parametrize("T,S,H", [(1, 4, 4096), (2, 4, 4096), (2, 8, 1024), (3, 4, 4096),
                                    (16, 3, 512), (17, 4, 4096), (40, 8, 1024),
                                    (130, 4, 4096), (129, 6, 512), (300, 2, 1056),
+                                   (256, 4, 4096), (65, 8, 1024),
                                    (257, 1, 64), (5, 4, 16384), (3, 2, 65536),
                                    (40, 1, 65536)])
 def test_exact_rows_equal_solo(mhc, T, S, H):
@@ -78,12 +79,14 @@ def test_exact_more_tokens_than_one_pass(mhc):
     _check(mhc, d, 20, 1e-6, [0, 8191, 8192, 8199], "T8200S1H32")
 
 
-def test_exact_matches_plain_call_on_small_batches(mhc):
-    # up to 16 tokens both entry points run the same kernels
-    c = CONFIGS["verify8"]
-    d = make_site(c)
-    print("[case] exact vs plain, verify8", flush=True)
-    for u, v in zip(_pre(mhc, d, c.iters, c.eps, True), _pre(mhc, d, c.iters, c.eps, False)):
+@pytest.mark.parametrize("T,S,H", [(8, 4, 4096), (255, 4, 4096), (200, 2, 1024), (64, 8, 1024),
+                                   (33, 6, 512)])
+def test_exact_matches_plain_call_below_the_large_batch_schedules(mhc, T, S, H):
+    # below 256 tokens (S <= 4) or up to 64 (S > 4) both entry points run the
+    # same kernels with the solo K-split
+    d = make_random_shape(T, S, H, seed=7 * T + S)
+    print(f"[case] exact vs plain T{T}S{S}H{H}", flush=True)
+    for u, v in zip(_pre(mhc, d, 20, 1e-6, True), _pre(mhc, d, 20, 1e-6, False)):
         assert np.array_equal(u, v)
 
 

@@ -35,7 +35,8 @@ def _alloc(T, S, H):
     return (e(T, S), e(T, S), e(T, S, S), e(T, H)), e(T, S, H)
 
 
-@pytest.mark.parametrize("T,S,H", [(1, 4, 4096), (2, 8, 512), (8, 4, 4096), (130, 4, 1024)])
+@pytest.mark.parametrize("T,S,H", [(1, 4, 4096), (2, 8, 512), (8, 4, 4096), (130, 4, 1024),
+                                   (258, 4, 1024)])
 def test_graph_replays_match_eager(mhc, T, S, H):
     print(f"[case] graph T={T} S={S} H={H}", flush=True)
     iters, eps = 20, 1e-6

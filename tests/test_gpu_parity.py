@@ -96,9 +96,12 @@ def test_config_parity_full_size_sampled(mhc, name):
     (1, 1, 4, 1), (2, 2, 8, 3), (3, 3, 12, 20), (5, 4, 132, 20), (16, 4, 4096, 20),
     (17, 4, 260, 7), (33, 5, 36, 20), (70, 6, 52, 20), (19, 7, 1028, 20),
     (9, 8, 7168, 20), (130, 8, 40, 20), (257, 2, 1000, 20), (40, 1, 8196, 50),
-    # batches large enough for the token-tiled fused kernel (S <= 4)
+    # mid-size batches on the solo K-split (S <= 4, T < 256)
     (127, 4, 4096, 20), (128, 4, 4096, 20), (131, 3, 1028, 20), (129, 4, 68, 20),
-    (200, 1, 8192, 20), (300, 2, 4, 5), (133, 4, 2052, 1),
+    (200, 1, 8192, 20), (255, 2, 4, 5),
+    # batches large enough for the token-tiled fused kernel (S <= 4, T >= 256)
+    (256, 4, 4096, 20), (259, 3, 1028, 20), (300, 2, 4, 5), (261, 4, 2052, 1),
+    (257, 4, 68, 20), (320, 1, 8192, 20),
 ])
 def test_ragged_shapes(mhc, T, S, H, iters):
     _say(f"ragged T={T} S={S} H={H} iters={iters}")

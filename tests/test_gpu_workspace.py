@@ -70,7 +70,8 @@ def _walk_ws(mhc, ws, T, sites, nw=None, record=True):
 
 
 @pytest.mark.parametrize("T,S,H,maxT", [(1, 4, 4096, 1), (2, 4, 4096, 4), (7, 3, 1024, 16),
-                                        (1, 8, 1024, 2), (130, 4, 4096, 130)])
+                                        (1, 8, 1024, 2), (130, 4, 4096, 130),
+                                        (256, 4, 4096, 260)])
 def test_ws_walk_equals_allocating_walk(mhc, T, S, H, maxT):
     print(f"[case] workspace walk T{T} S{S} H{H} max_tokens {maxT}", flush=True)
     x0, sites = _sites(T, S, H, 4, seed=T + S)

@@ -71,11 +71,12 @@ def test_zq8_prefill_sampled(mhc):
 
 
 # Paths: T <= 2 and S <= 4 run the epilogue in the single-launch decode kernel
-# while y fits its registers (T*H <= 9216), T >= 128 with an on-chip slab in the
+# while y fits its registers (T*H <= 9216), T >= 256 with an on-chip slab in the
 # fused kernel's tail, everything else as a launch of its own.
 @pytest.mark.parametrize("T,S,H", [(1, 1, 32), (1, 4, 8192), (2, 4, 4096), (2, 3, 4608),
                                    (2, 4, 8192), (2, 8, 7168), (3, 2, 64), (17, 4, 1024),
                                    (128, 2, 1056), (130, 4, 4096), (131, 1, 8192),
+                                   (256, 2, 1056), (258, 4, 4096), (259, 1, 8192),
                                    (129, 3, 8192)])
 def test_zq8_shapes(mhc, T, S, H):
     d = make_random_shape(T, S, H, seed=T + 5 * S)
