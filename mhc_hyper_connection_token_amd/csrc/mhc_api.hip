@@ -242,19 +242,14 @@ int site_pre_run(const float* x, const float* fn_w, const float* scale, const fl
     if ((rc = acquire_scratch(src, p.part_floats * sizeof(float), &sc))) return rc;
     float* part = sc.general;
     hipError_t e;
-    if (T <= 2) {
-      // decode sizes: one launch; the block that draws the last ticket finishes
-      if (mhc::decode4_supported(T, S, p.G)) {
-        const bool fuse = zq && mhc::decode4_zq8_supported(T, H);
-        e = mhc::launch_decode4_pre(x, fn_w, scale, base, T, S, H, iters, eps, p.G, p.cpr, part,
-                                    sc.counter, pre, post, comb, y, fuse ? zq : nullptr, st);
-        zq_done = fuse;
-      } else {
-        e = mhc::launch_decode_pre(x, fn_w, scale, base, T, S, H, iters, eps, p.G, p.cpr, part,
-                                   sc.counter, pre, post, comb, y, st);
-      }
+    if (zq && mhc::decode_zq8_supported(T, S, H, p.G)) {
+      // one decode token with the epilogue: one launch; the block that draws
+      // the last ticket finishes
+      e = mhc::launch_decode_zq8(x, fn_w, scale, base, T, S, H, iters, eps, p.G, p.cpr, part,
+                                 sc.counter, pre, post, comb, y, *zq, st);
+      zq_done = true;
     } else {
-      // S <= 4 below the fused threshold: the decode kernels' vector-ALU partials
+      // S <= 4 below the fused threshold: the vector-ALU partials
       e = (S <= 4 && T < kFusedMinTokens)
               ? mhc::launch_small_partials(x, fn_w, T, S, H, p.G, p.cpr, part, st)
               : mhc::launch_partials(x, fn_w, T, n, R, p.ntt, p.G, p.cpr, part, st);
@@ -291,15 +286,15 @@ int mhc_site_pre_exact(const float* x, const float* fn_w, const float* scale, co
                               comb, y);
   if (rc || T == 0) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // One or two tokens: the single-launch decode kernels, which define the solo result.
-  if (T <= 2)
-    return site_pre_run(x, fn_w, scale, base, T, streams, hidden, iters, eps, pre, post, comb, y,
-                        nullptr, st);
-  // Otherwise the split path with the K-split of a solo token: partials in the
-  // decode kernels' per-token order (vector ALU for S <= 4, 16-token MFMA tiles
-  // above), then the finish kernel, whose reduction order is the decode
-  // kernels' own.  Tokens go in chunks so that the partials stay bounded.
   const int S = streams, H = hidden, n = S * H, R = (2 + S) * S;
+  // Where the plain call keeps the solo K-split it is already exact.
+  if (S <= 4 ? T < kFusedMinTokens : T <= kSoloPlanMaxWide)
+    return site_pre_run(x, fn_w, scale, base, T, S, H, iters, eps, pre, post, comb, y, nullptr,
+                        st);
+  // Otherwise the same split path with the solo K-split at any T: partials in
+  // the per-token order of a solo call (vector ALU for S <= 4, 16-token MFMA
+  // tiles above), then the finish kernel.  Tokens go in chunks so that the
+  // partials stay bounded.
   const PrePlan p1 = plan_pre(1, S, H);
   const int chunk = T < kExactChunk ? T : kExactChunk;
   Scratch sc;

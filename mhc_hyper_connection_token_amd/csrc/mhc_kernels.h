@@ -41,25 +41,16 @@ hipError_t launch_fused_pre(const float* x, const float* fn_w, const float* scal
                             float* pre, float* post, float* comb, float* y, float* wpack,
                             const Zq8Out* zq, hipStream_t st);
 
-// Single-launch pre chain for T <= 2: split-K partials into `part`, last block
-// (ticket on `counter`, which must be zero on entry and is zero again on exit)
-// finishes.  Same G / chunks_per_range as the two-kernel path.
-hipError_t launch_decode_pre(const float* x, const float* fn_w, const float* scale,
+// Single-launch pre chain and branch-input epilogue of one token (S <= 4,
+// H % 32 == 0; decode_zq8_supported): split-K partials into `part` (same G /
+// chunks_per_range as the two-kernel path), the last block (ticket on
+// `counter`, which must be zero on entry and is zero again on exit) finishes.
+bool decode_zq8_supported(int T, int S, int H, int G);
+hipError_t launch_decode_zq8(const float* x, const float* fn_w, const float* scale,
                              const float* base, int T, int S, int H, int iters, float eps, int G,
-                             int chunks_per_range, float* part, unsigned int* counter,
-                             float* pre, float* post, float* comb, float* y, hipStream_t st);
-
-// Single-launch pre chain for T <= 2 and S <= 4 (same ticket contract), with
-// the collapse operands requested while the partials are being added.  With zq
-// non-null the last block also writes the branch-input epilogue; that needs
-// decode4_zq8_supported(T, H).
-bool decode4_supported(int T, int S, int G);
-bool decode4_zq8_supported(int T, int H);
-hipError_t launch_decode4_pre(const float* x, const float* fn_w, const float* scale,
-                              const float* base, int T, int S, int H, int iters, float eps,
-                              int G, int chunks_per_range, float* part, unsigned int* counter,
-                              float* pre, float* post, float* comb, float* y, const Zq8Out* zq,
-                              hipStream_t st);
+                             int chunks_per_range, float* part, unsigned int* counter, float* pre,
+                             float* post, float* comb, float* y, const Zq8Out& zq,
+                             hipStream_t st);
 
 // Branch-input epilogue: z = RMS-norm(y) * nw and its q8 codes / block scales,
 // one block per token; H % 32 == 0 and H <= 8192 (zq8_supported).

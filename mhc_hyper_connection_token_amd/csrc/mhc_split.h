@@ -439,55 +439,4 @@ __device__ __forceinline__ void reduce_token_partials(const float* __restrict__ 
   __syncthreads();
 }
 
-// The same fixed-order sum as reduce_token_partials (bit-identical result), done
-// by ONE wavefront: lane l plays threads l, l + 64, l + 128 and l + 192 of the
-// 256-thread version, with all of their loads of a batch in flight together.
-// LDS accesses of one wavefront complete in order, so no barrier is needed;
-// only m_out (in LDS) is written for the rest of the block, which must
-// synchronise before reading it.
-template <bool COHERENT = false, int BATCH = 16>
-__device__ __forceinline__ void reduce_token_partials_wave(const float* __restrict__ part, int G,
-                                                           int T, int t, int RP, float* red256,
-                                                           float* m_out) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int Q = 256 / RP;
-  const int QR = Q * RP;
-  const float* p = part + (size_t)t * RP;
-  const size_t gstride = (size_t)T * RP;
-  float s[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int g0 = 0; g0 < G; g0 += BATCH * Q) {
-    float v[4][BATCH];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tid = lane + kWave * i;
-      const int tc = tid < QR ? tid : lane;  // lane < 64 <= QR is always valid
-      const int r = tc % RP, q = tc / RP;
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const int g = g0 + q + u * Q;
-        v[i][u] = load_partial<COHERENT>(p + r + (size_t)(g < G ? g : q) * gstride);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tid = lane + kWave * i;
-      const int q = (tid < QR ? tid : lane) / RP;
-#pragma unroll
-      for (int u = 0; u < BATCH; ++u)
-        if (g0 + q + u * Q < G) s[i] += v[i][u];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tid = lane + kWave * i;
-    if (tid < QR) red256[tid] = s[i];
-  }
-  __builtin_amdgcn_wave_barrier();
-  if (lane < RP) {
-    float sum = 0.f;
-    for (int q = 0; q < Q; ++q) sum += red256[q * RP + lane];
-    m_out[lane] = sum;
-  }
-}
-
 }  // namespace mhc

@@ -70,9 +70,9 @@ def test_zq8_prefill_sampled(mhc):
     _check(mhc, make_site(c), c.iters, c.eps, "prefill", tokens=toks)
 
 
-# Paths: T <= 2 and S <= 4 run the epilogue in the single-launch decode kernel
-# while y fits its registers (T*H <= 9216), T >= 256 with an on-chip slab in the
-# fused kernel's tail, everything else as a launch of its own.
+# Paths: one token with S <= 4 runs the epilogue in the single-launch decode
+# kernel, T >= 256 with an on-chip slab in the fused kernel's tail, everything
+# else as a launch of its own after the split path.
 @pytest.mark.parametrize("T,S,H", [(1, 1, 32), (1, 4, 8192), (2, 4, 4096), (2, 3, 4608),
                                    (2, 4, 8192), (2, 8, 7168), (3, 2, 64), (17, 4, 1024),
                                    (128, 2, 1056), (130, 4, 4096), (131, 1, 8192),
