@@ -64,6 +64,13 @@ def _load():
         lib.mhc_oracle_q8.argtypes = [fp, ctypes.c_long, ctypes.c_int,
                                       ctypes.POINTER(ctypes.c_int8), fp]
         lib.mhc_oracle_q8.restype = ctypes.c_int
+        lib.mhc_oracle_expand.argtypes = [fp, ctypes.c_long, ctypes.c_int, ctypes.c_int, fp]
+        lib.mhc_oracle_expand.restype = ctypes.c_int
+        lib.mhc_oracle_mean.argtypes = [fp, ctypes.c_long, ctypes.c_int, ctypes.c_int, dp]
+        lib.mhc_oracle_mean.restype = ctypes.c_int
+        lib.mhc_oracle_head.argtypes = [fp, fp, fp, fp, ctypes.c_long, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_double, dp, dp]
+        lib.mhc_oracle_head.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -174,3 +181,44 @@ def q8(z):
     if lib.mhc_oracle_q8(pz, T, H, q.ctypes.data_as(ctypes.POINTER(ctypes.c_int8)), pd) != 0:
         raise ValueError("mhc_oracle_q8 rejected its arguments")
     return q, d
+
+
+def expand(e, S: int):
+    """O10: the trunk entry, e [T, H] float32 -> x [T, S, H] float32 (a copy into
+    every stream)."""
+    lib = _load()
+    e, pe = _f32(e)
+    T, H = e.shape
+    x, px = _f32(np.empty((T, S, H), dtype=np.float32))
+    if lib.mhc_oracle_expand(pe, T, S, H, px) != 0:
+        raise ValueError("mhc_oracle_expand rejected its arguments")
+    return x
+
+
+def mean(x):
+    """O11: the unweighted stream mean, x [T, S, H] float32 -> y [T, H] float64."""
+    lib = _load()
+    x, px = _f32(x)
+    T, S, H = x.shape
+    y, py = _f64(np.empty((T, H)))
+    if lib.mhc_oracle_mean(px, T, S, H, py) != 0:
+        raise ValueError("mhc_oracle_mean rejected its arguments")
+    return y
+
+
+def head(x, fn_h, scale_h, base_h, eps: float):
+    """O12: the gated-head exit.  x [T, S, H], fn_h [S, S*H], scale_h [1], base_h [S]
+    (float32) -> {"gates": [T, S], "y": [T, H]} in float64."""
+    lib = _load()
+    x, px = _f32(x)
+    T, S, H = x.shape
+    fn_h, pw = _f32(fn_h)
+    scale_h, ps = _f32(np.asarray(scale_h).reshape(1))
+    base_h, pb = _f32(base_h)
+    if fn_h.shape != (S, S * H) or base_h.shape != (S,):
+        raise ValueError("head weight must be [S, S*H] and bias [S]")
+    g, pg = _f64(np.empty((T, S)))
+    y, py = _f64(np.empty((T, H)))
+    if lib.mhc_oracle_head(px, pw, ps, pb, T, S, H, float(eps), pg, py) != 0:
+        raise ValueError("mhc_oracle_head rejected its arguments")
+    return {"gates": g, "y": y}

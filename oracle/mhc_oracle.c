@@ -304,3 +304,73 @@ int mhc_oracle_sinkhorn(const double *z, int S, int iters, double eps,
   sinkhorn(comb, S, iters, eps);
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Trunk entry and exit (hyper.rs page: the doc comments of `expand`,
+ * `contract_mean` and `collapse`, and the HyperHead loader, which sizes the
+ * head's weight [S][S*H], its bias [S] and a single scale).  The page gives the
+ * shapes and the kernel names but not the formulas; the readings taken are:
+ *   O10 expand: x[t,k,i] = e[t,i] for every stream k (the entry copies the
+ *       embedding into each stream; the page calls the mean kernel its
+ *       inverse, and the mean of S equal copies is the copy).
+ *   O11 mean:   y[t,i] = (sum_k x[t,k,i]) / S, streams in ascending order.
+ *   O12 gated head ("sigmoid-gated pre-only collapse"): the pre half of a site
+ *       with the head's own S rows, one scale and S biases:
+ *         rinv = 1/sqrt(sum_i x[t,i]^2 / (S*H) + eps)          (as O1)
+ *         m_c  = rinv * sum_i fn_h[c,i] * x[t,i]                c < S
+ *         g_c  = 1/(1+exp(-(scale_h * m_c + base_c)))          (the pre gate form)
+ *         y[t,i] = sum_c g_c * x[t,c,i]                         (as O6)
+ */
+
+/* O10: e [T][H] -> x [T][S][H]; a copy, exact. */
+int mhc_oracle_expand(const float *e, long T, int S, int H, float *x) {
+  if (T < 0 || S < 1 || H < 1) return 1;
+  if (T == 0) return 0;
+  if (!e || !x) return 1;
+  for (long t = 0; t < T; ++t)
+    for (int k = 0; k < S; ++k)
+      for (int i = 0; i < H; ++i) x[(t * S + k) * H + i] = e[t * H + i];
+  return 0;
+}
+
+/* O11: x [T][S][H] -> y [T][H] (double). */
+int mhc_oracle_mean(const float *x, long T, int S, int H, double *y) {
+  if (T < 0 || S < 1 || H < 1) return 1;
+  if (T == 0) return 0;
+  if (!x || !y) return 1;
+  for (long t = 0; t < T; ++t)
+    for (int i = 0; i < H; ++i) {
+      double acc = 0.0;
+      for (int k = 0; k < S; ++k) acc += (double)x[(t * S + k) * H + i];
+      y[t * H + i] = acc / (double)S;
+    }
+  return 0;
+}
+
+/* O12: x [T][S][H], fn_h [S][S*H], scale_h [1], base_h [S] -> gates [T][S],
+ * y [T][H] (double). */
+int mhc_oracle_head(const float *x, const float *fn_h, const float *scale_h,
+                    const float *base_h, long T, int S, int H, double eps,
+                    double *gates, double *y) {
+  if (T < 0 || S < 1 || S > 8 || H < 1 || !(eps > 0.0)) return 1;
+  if (T == 0) return 0;
+  if (!x || !fn_h || !scale_h || !base_h || !gates || !y) return 1;
+  const long n = (long)S * H;
+  for (long t = 0; t < T; ++t) {
+    const float *xt = x + t * n;
+    double ss = 0.0;
+    for (long i = 0; i < n; ++i) ss += (double)xt[i] * (double)xt[i];
+    const double rinv = 1.0 / sqrt(ss / (double)n + eps);
+    double g[8];
+    for (int c = 0; c < S; ++c) {
+      const float *w = fn_h + (long)c * n;
+      double acc = 0.0;
+      for (long i = 0; i < n; ++i) acc += (double)xt[i] * (double)w[i];
+      const double z = (double)scale_h[0] * (rinv * acc) + (double)base_h[c];
+      g[c] = 1.0 / (1.0 + exp(-z));
+      gates[t * S + c] = g[c];
+    }
+    token_collapse(xt, g, S, H, y + t * H);
+  }
+  return 0;
+}

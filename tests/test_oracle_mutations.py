@@ -71,6 +71,24 @@ MUTANTS = {
     "q8 truncates": lambda s: s.replace("(signed char)roundf(v)", "(signed char)v"),
     "q8 blocks of 16": lambda s: s.replace("const float *zb = z + t * H + b * 32;",
                                            "const float *zb = z + t * H + b * 16;"),
+    "expand fills only the first stream": lambda s: s.replace(
+        "x[(t * S + k) * H + i] = e[t * H + i];",
+        "x[(t * S + k) * H + i] = k == 0 ? e[t * H + i] : 0.0f;"),
+    "mean divides by S + 1": lambda s: s.replace(
+        "y[t * H + i] = acc / (double)S;", "y[t * H + i] = acc / (double)(S + 1);"),
+    "mean skips the last stream": lambda s: s.replace(
+        "for (int k = 0; k < S; ++k) acc += (double)x[(t * S + k) * H + i];",
+        "for (int k = 0; k < S - 1; ++k) acc += (double)x[(t * S + k) * H + i];"),
+    "head gate without the RMS rescale": lambda s: s.replace(
+        "(double)scale_h[0] * (rinv * acc) + (double)base_h[c];",
+        "(double)scale_h[0] * acc + (double)base_h[c];"),
+    "head scale multiplies the bias too": lambda s: s.replace(
+        "(double)scale_h[0] * (rinv * acc) + (double)base_h[c];",
+        "(double)scale_h[0] * ((rinv * acc) + (double)base_h[c]);"),
+    "head sigmoid sign flipped": lambda s: s.replace(
+        "g[c] = 1.0 / (1.0 + exp(-z));", "g[c] = 1.0 / (1.0 + exp(z));"),
+    "head weight rows offset by one": lambda s: s.replace(
+        "const float *w = fn_h + (long)c * n;", "const float *w = fn_h + (long)(c + 1) % S * n;"),
 }
 
 

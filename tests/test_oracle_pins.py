@@ -491,3 +491,101 @@ def test_q8_ties_round_away_from_zero_and_zero_blocks():
     assert d[0, 0] == 1.0 and d[0, 1] == 0.0
     assert list(q[0, :5]) == [127, 3, -3, 1, 0]
     assert np.all(q[0, 32:] == 0)   # an all-zero block: d = 0 and all codes 0
+
+
+# ------------------------------------------------------------------ trunk entry and exit
+# O10 (expand), O11 (mean), O12 (gated head): hyper.rs page, doc comments of
+# `expand`, `contract_mean` and `collapse`, and the HyperHead loader (weight
+# [S][S*H], bias [S], one scale).  The page names the kernels and shapes only;
+# the pins fix what the readings mean.
+@pytest.mark.parametrize("S", [1, 3, 4, 8])
+def test_expand_copies_the_embedding_into_every_stream(S):
+    rng = np.random.default_rng(S)
+    e = rng.standard_normal((5, 24)).astype(np.float32)
+    x = oracle.expand(e, S)
+    assert x.shape == (5, S, 24)
+    for k in range(S):
+        assert np.array_equal(x[:, k, :], e)
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 5, 8])
+def test_mean_inverts_expand_exactly(S):
+    # the page calls the mean kernel the inverse of the entry; S equal copies
+    # summed in double are exact, and so is the division by S
+    rng = np.random.default_rng(10 + S)
+    e = rng.standard_normal((3, 40)).astype(np.float32)
+    assert np.array_equal(oracle.mean(oracle.expand(e, S)), e.astype(np.float64))
+
+
+def test_mean_known_values_and_brute_force():
+    S, H = 4, 6
+    x = np.zeros((1, S, H), dtype=np.float32)
+    for k in range(S):
+        x[0, k, :] = k
+    assert np.all(oracle.mean(x) == 1.5)  # (0 + 1 + 2 + 3) / 4
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((2, 3, 10)).astype(np.float32)
+    y = oracle.mean(x)
+    getcontext().prec = 40
+    for t in range(2):
+        for i in range(10):
+            want = sum((Decimal(float(x[t, k, i])) for k in range(3)), Decimal(0)) / 3
+            assert abs(y[t, i] - float(want)) <= 1e-15 * max(1.0, abs(float(want)))
+
+
+def _head_case(T, S, H, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.uniform(-1, 1, (T, S, H)).astype(np.float32)
+    w = (rng.standard_normal((S, S * H)) / np.sqrt(S * H)).astype(np.float32)
+    return x, w
+
+
+def test_head_with_a_sites_pre_rows_gives_that_sites_pre_gates_and_branch_input():
+    # the head is the pre half of a site with its own S rows, one scale and S
+    # biases: fed a site's pre rows, scale and biases it must reproduce that
+    # site's pre gates and collapse (the site oracle is pinned on its own above)
+    d = _site(3, 4, 64, seed=21)
+    S = 4
+    o = oracle.site_pre(d["x"], d["fn_w"], d["scale"], d["base"], 20, 1e-6)
+    h = oracle.head(d["x"], d["fn_w"][:S], d["scale"][:1], d["base"][:S], 1e-6)
+    np.testing.assert_allclose(h["gates"], o["pre"], rtol=1e-13, atol=0)
+    np.testing.assert_allclose(h["y"], o["y"], rtol=1e-12, atol=1e-15)
+
+
+def test_head_closed_forms_zero_weight_and_saturation():
+    T, S, H = 2, 3, 16
+    x, _ = _head_case(T, S, H, 4)
+    w = np.zeros((S, S * H), dtype=np.float32)
+    base = np.array([0.3, -1.2, 2.0], dtype=np.float32)
+    h = oracle.head(x, w, np.array([0.7], np.float32), base, 1e-6)
+    g = 1.0 / (1.0 + np.exp(-base.astype(np.float64)))  # the scale multiplies m = 0 only
+    np.testing.assert_allclose(h["gates"], np.tile(g, (T, 1)), rtol=1e-15)
+    want = np.einsum("c,tci->ti", g, x.astype(np.float64))
+    np.testing.assert_allclose(h["y"], want, rtol=1e-13, atol=1e-15)
+    # saturated biases pick one stream exactly
+    h = oracle.head(x, w, np.array([1.0], np.float32),
+                    np.array([-800.0, 800.0, -800.0], np.float32), 1e-6)
+    assert np.array_equal(h["gates"], np.tile([0.0, 1.0, 0.0], (T, 1)))
+    assert np.array_equal(h["y"], x[:, 1, :].astype(np.float64))
+
+
+def test_head_matches_high_precision_brute_force():
+    T, S, H = 2, 2, 5
+    x, w = _head_case(T, S, H, 9)
+    scale, base, eps = np.float32(1.3), np.array([0.2, -0.4], np.float32), 1e-6
+    h = oracle.head(x, w, np.array([scale]), base, eps)
+    getcontext().prec = 40
+    n = S * H
+    for t in range(T):
+        xs = [Decimal(float(v)) for v in x[t].reshape(-1)]
+        ss = sum((v * v for v in xs), Decimal(0))
+        rinv = 1 / (ss / n + Decimal(eps)).sqrt()
+        gates = []
+        for c in range(S):
+            dot = sum((Decimal(float(a)) * b for a, b in zip(w[c], xs)), Decimal(0))
+            z = Decimal(float(scale)) * rinv * dot + Decimal(float(base[c]))
+            gates.append(1 / (1 + (-z).exp()))
+        np.testing.assert_allclose(h["gates"][t], [float(g) for g in gates], rtol=1e-14)
+        for i in range(H):
+            want = sum((gates[c] * xs[c * H + i] for c in range(S)), Decimal(0))
+            assert abs(h["y"][t, i] - float(want)) <= 1e-14 * max(1.0, abs(float(want)))
