@@ -150,6 +150,33 @@ int mhc_site_pre_zq8(const float* x, const float* fn_w, const float* scale, cons
                      signed char* q, float* d, void* stream);
 
 /*
+ * Trunk entry and exit (hyper.rs page: doc comments of `expand`,
+ * `contract_mean` and `collapse`; the HyperHead loader sizes the head).
+ *
+ * mhc_expand: x_out[t,k,i] = e[t,i] for every stream k.
+ *   e [T][H] (read only) -> x_out [T][S][H]; x_out must not overlap e.
+ * mhc_mean: y_out[t,i] = (sum_k x[t,k,i]) / S, streams summed in ascending
+ *   order in fp32, then one IEEE division.  x [T][S][H] -> y_out [T][H].
+ * mhc_head: the gated-head exit, the pre half of a site with the head's own
+ *   weight fn_w [S][S*H], one scale [1] and biases base [S]:
+ *     rinv = 1/sqrt(sum_i x[t,i]^2 / (S*H) + eps)         (over the slab)
+ *     gates[t,c] = 1/(1+exp(-(scale * rinv * (fn_w[c,:] . x[t,:]) + base[c])))
+ *     y[t,i] = sum_c gates[t,c] * x[t,c,i]
+ *   gates [T][S] and y [T][H] are outputs; they must not overlap the inputs or
+ *   each other.  Uses the library's per-device scratch (as mhc_site_pre).
+ * Same size, pointer and return-code conventions as the site calls (hidden % 4
+ * == 0, 16-byte aligned pointers, 1 <= streams <= 8, eps > 0 and finite;
+ * T = 0 does nothing).  mhc_head_check is the host-side check alone.
+ */
+int mhc_expand(const float* e, int T, int streams, int hidden, float* x_out, void* stream);
+int mhc_mean(const float* x, int T, int streams, int hidden, float* y_out, void* stream);
+int mhc_head(const float* x, const float* fn_w, const float* scale, const float* base, int T,
+             int streams, int hidden, float eps, float* gates, float* y, void* stream);
+int mhc_head_check(const float* x, const float* fn_w, const float* scale, const float* base,
+                   int T, int streams, int hidden, float eps, const float* gates,
+                   const float* y);
+
+/*
  * Persistent site workspace (the hyper.rs page, doc comment of HyperDecodeWs:
  * one set of buffers per engine, every buffer fully overwritten before it is
  * read, the stream state ping-ponged with one spare slot, so that a decode

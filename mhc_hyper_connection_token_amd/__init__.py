@@ -18,8 +18,9 @@ import ctypes
 import os
 
 __all__ = ["site_pre", "site_post", "site_pre_zq8", "site_pre_check", "site_post_check",
-           "site_pre_zq8_check", "Workspace", "workspace_bytes", "load_library", "MhcError",
-           "LIB_PATH", "EXPORTED_SYMBOLS", "STATUS"]
+           "site_pre_zq8_check", "expand", "mean", "head", "head_check", "Workspace",
+           "workspace_bytes", "load_library", "MhcError", "LIB_PATH", "EXPORTED_SYMBOLS",
+           "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmhc.so")
@@ -28,6 +29,7 @@ EXPORTED_SYMBOLS = ("mhc_site_pre", "mhc_site_post", "mhc_site_pre_exact", "mhc_
                     "mhc_site_pre_check", "mhc_site_post_check", "mhc_site_pre_zq8_check",
                     "mhc_workspace_bytes", "mhc_workspace_struct_bytes", "mhc_workspace_init",
                     "mhc_ws_site_pre", "mhc_ws_site_pre_zq8", "mhc_ws_site_post",
+                    "mhc_expand", "mhc_mean", "mhc_head", "mhc_head_check",
                     "mhc_status_string")
 
 STATUS = {0: "MHC_OK", 1: "MHC_EINVAL", 2: "MHC_EALIGN", 3: "MHC_EUNSUPPORTED",
@@ -83,6 +85,14 @@ def load_library() -> ctypes.CDLL:
     lib.mhc_ws_site_pre_zq8.restype = i
     lib.mhc_ws_site_post.argtypes = [wsp, vp, i, vp]
     lib.mhc_ws_site_post.restype = i
+    lib.mhc_expand.argtypes = [vp, i, i, i, vp, vp]
+    lib.mhc_expand.restype = i
+    lib.mhc_mean.argtypes = [vp, i, i, i, vp, vp]
+    lib.mhc_mean.restype = i
+    lib.mhc_head.argtypes = [vp, vp, vp, vp, i, i, i, fl, vp, vp, vp]
+    lib.mhc_head.restype = i
+    lib.mhc_head_check.argtypes = [vp, vp, vp, vp, i, i, i, fl, vp, vp]
+    lib.mhc_head_check.restype = i
     if lib.mhc_workspace_struct_bytes() != ctypes.sizeof(_WsStruct):
         raise RuntimeError("mhc_workspace layout of the library and the binding differ")
     _lib = lib
@@ -223,6 +233,70 @@ def site_pre_zq8_check(x_ptr, fn_w_ptr, scale_ptr, base_ptr, nw_ptr, T, S, H, it
     return lib.mhc_site_pre_zq8_check(x_ptr, fn_w_ptr, scale_ptr, base_ptr, nw_ptr, T, S, H,
                                       iters, float(eps), float(norm_eps), pre_ptr, post_ptr,
                                       comb_ptr, y_ptr, z_ptr, q_ptr, d_ptr)
+
+
+def expand(e, streams: int, *, out=None, stream=None):
+    """Trunk entry: e [T, H] -> x [T, S, H] (a copy of e in every stream)."""
+    import torch
+    lib = load_library()
+    if e.dim() != 2:
+        raise ValueError("e must be [T, H]")
+    T, H = e.shape
+    pe = _dev(e, "e")
+    if out is None:
+        out = torch.empty((T, streams, H), device=e.device, dtype=torch.float32)
+    po = _dev(out, "out", (T, streams, H))
+    rc = lib.mhc_expand(pe, T, streams, H, po, _stream_handle(stream))
+    if rc != 0:
+        raise MhcError("mhc_expand", rc, _status_text(lib, rc))
+    return out
+
+
+def mean(x, *, out=None, stream=None):
+    """Trunk exit (unweighted): x [T, S, H] -> y [T, H], the mean over the streams."""
+    import torch
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be [T, S, H]")
+    T, S, H = x.shape
+    px = _dev(x, "x")
+    if out is None:
+        out = torch.empty((T, H), device=x.device, dtype=torch.float32)
+    po = _dev(out, "out", (T, H))
+    rc = lib.mhc_mean(px, T, S, H, po, _stream_handle(stream))
+    if rc != 0:
+        raise MhcError("mhc_mean", rc, _status_text(lib, rc))
+    return out
+
+
+def head(x, fn_w, scale, base, eps: float, *, out=None, stream=None):
+    """Trunk exit (gated head): x [T, S, H], fn_w [S, S*H], scale [1], base [S] ->
+    (gates [T, S], y [T, H]); `out` may supply that pair."""
+    import torch
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be [T, S, H]")
+    T, S, H = x.shape
+    px = _dev(x, "x")
+    pw = _dev(fn_w, "fn_w", (S, S * H))
+    ps = _dev(scale, "scale", (1,))
+    pb = _dev(base, "base", (S,))
+    if out is None:
+        out = (torch.empty((T, S), device=x.device, dtype=torch.float32),
+               torch.empty((T, H), device=x.device, dtype=torch.float32))
+    g, y = out
+    rc = lib.mhc_head(px, pw, ps, pb, T, S, H, float(eps), _dev(g, "gates", (T, S)),
+                      _dev(y, "y", (T, H)), _stream_handle(stream))
+    if rc != 0:
+        raise MhcError("mhc_head", rc, _status_text(lib, rc))
+    return out
+
+
+def head_check(x_ptr, fn_w_ptr, scale_ptr, base_ptr, T, S, H, eps, gates_ptr, y_ptr) -> int:
+    """The library's host-side argument check of mhc_head on raw addresses."""
+    lib = load_library()
+    return lib.mhc_head_check(x_ptr, fn_w_ptr, scale_ptr, base_ptr, T, S, H, float(eps),
+                              gates_ptr, y_ptr)
 
 
 def workspace_bytes(max_tokens: int, streams: int, hidden: int) -> int:

@@ -375,6 +375,83 @@ int mhc_site_post(const float* x, const float* f, const float* post, const float
 
 }  // extern "C"
 
+// ---------------------------------------------------------------- trunk ends
+extern "C" {
+
+int mhc_expand(const float* e, int T, int streams, int hidden, float* x_out, void* stream) {
+  int rc = check_shape(T, streams, hidden);
+  if (rc || T == 0) return rc;
+  if ((rc = check_ptr(e)) || (rc = check_ptr(x_out))) return rc;
+  const size_t Tz = T, S = streams, H = hidden;
+  if (overlaps(span(x_out, Tz * S * H * 4), span(e, Tz * H * 4))) return MHC_EOVERLAP;
+  return mhc::launch_expand(e, T, streams, hidden, x_out, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? MHC_OK
+             : MHC_EHIP;
+}
+
+int mhc_mean(const float* x, int T, int streams, int hidden, float* y_out, void* stream) {
+  int rc = check_shape(T, streams, hidden);
+  if (rc || T == 0) return rc;
+  if ((rc = check_ptr(x)) || (rc = check_ptr(y_out))) return rc;
+  const size_t Tz = T, S = streams, H = hidden;
+  if (overlaps(span(y_out, Tz * H * 4), span(x, Tz * S * H * 4))) return MHC_EOVERLAP;
+  return mhc::launch_mean(x, T, streams, hidden, y_out, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? MHC_OK
+             : MHC_EHIP;
+}
+
+int mhc_head_check(const float* x, const float* fn_w, const float* scale, const float* base,
+                   int T, int streams, int hidden, float eps, const float* gates,
+                   const float* y) {
+  int rc = check_shape(T, streams, hidden);
+  if (rc) return rc;
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return MHC_EINVAL;
+  if (T == 0) return MHC_OK;
+  const void* ptrs[] = {x, fn_w, scale, base, gates, y};
+  for (const void* p : ptrs)
+    if (!p) return MHC_EINVAL;
+  for (const void* p : ptrs)
+    if ((rc = check_ptr(p))) return rc;
+  const size_t S = streams, H = hidden, Tz = T;
+  const Span in[] = {span(x, Tz * S * H * 4), span(fn_w, S * S * H * 4), span(scale, 4),
+                     span(base, S * 4)};
+  const Span out[] = {span(gates, Tz * S * 4), span(y, Tz * H * 4)};
+  for (const Span& o : out)
+    for (const Span& i : in)
+      if (overlaps(o, i)) return MHC_EOVERLAP;
+  if (overlaps(out[0], out[1])) return MHC_EOVERLAP;
+  return MHC_OK;
+}
+
+int mhc_head(const float* x, const float* fn_w, const float* scale, const float* base, int T,
+             int streams, int hidden, float eps, float* gates, float* y, void* stream) {
+  int rc = mhc_head_check(x, fn_w, scale, base, T, streams, hidden, eps, gates, y);
+  if (rc || T == 0) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // The site's solo K-split over the same slab, S rows, in passes of at most
+  // kExactChunk tokens so that the partials stay bounded.
+  const int S = streams, H = hidden, n = S * H;
+  const PrePlan p1 = plan_pre(1, S, H);
+  const int chunk = T < kExactChunk ? T : kExactChunk;
+  Scratch sc;
+  if ((rc = get_scratch((size_t)p1.G * chunk * (S + 1) * sizeof(float), &sc))) return rc;
+  for (int t0 = 0; t0 < T; t0 += chunk) {
+    const int tc = T - t0 < chunk ? T - t0 : chunk;
+    const float* xc = x + (size_t)t0 * n;
+    hipError_t e = mhc::launch_small_partials_rows(xc, fn_w, tc, n, S, p1.G, p1.cpr, sc.general,
+                                                   st);
+    if (e == hipSuccess)
+      e = mhc::launch_head_finish(xc, sc.general, p1.G, tc, S, H, scale, base, eps,
+                                  gates + (size_t)t0 * S, y + (size_t)t0 * H, st);
+    if (e != hipSuccess) return MHC_EHIP;
+  }
+  return MHC_OK;
+}
+
+}  // extern "C"
+
 // ---------------------------------------------------------------- workspace
 // Caller memory carved into 256-byte aligned regions, in this order: the kernel
 // scratch (ticket header + the largest partials / packed weight of any

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void finish_kernel(
   }
 
   // 1. fixed-order reduction of the G partials
-  reduce_token_partials(part, G, T, t, RP, red, m_raw);
+  reduce_token_partials<false, 16>(part, G, T, t, RP, red, m_raw);
 
   // 2. pre gates, computed by every thread (uniform); only block hb == 0 runs
   // the Sinkhorn (wave 0, post and comb) and writes the gates.  No barrier

@@ -24,6 +24,9 @@ hipError_t launch_partials(const float* x, const float* fn_w, int T, int n, int 
 int small_rows_per_thread(int S);
 hipError_t launch_small_partials(const float* x, const float* fn_w, int T, int S, int H, int G,
                                  int chunks_per_range, float* part, hipStream_t st);
+// The same for any R <= 31 rows of a weight [R][n] (the head's R = S).
+hipError_t launch_small_partials_rows(const float* x, const float* fn_w, int T, int n, int R,
+                                      int G, int chunks_per_range, float* part, hipStream_t st);
 
 // Reduce partials, gates, Sinkhorn, collapse.
 hipError_t launch_finish(const float* x, const float* part, int G, int T, int S, int H,
@@ -57,6 +60,15 @@ hipError_t launch_decode_zq8(const float* x, const float* fn_w, const float* sca
 bool zq8_supported(int H);
 hipError_t launch_zq8(const float* y, const float* nw, int T, int H, float norm_eps, float* z,
                       signed char* q, float* d, hipStream_t st);
+
+// Trunk entry and exit: expand e [T][H] -> x [T][S][H]; mean x -> y [T][H];
+// the gated head's finish (partials of its S rows, from launch_small_partials_rows,
+// then gates [T][S] and y [T][H]).
+hipError_t launch_expand(const float* e, int T, int S, int H, float* x, hipStream_t st);
+hipError_t launch_mean(const float* x, int T, int S, int H, float* y, hipStream_t st);
+hipError_t launch_head_finish(const float* x, const float* part, int G, int T, int S, int H,
+                              const float* scale_h, const float* base_h, float eps, float* gates,
+                              float* y, hipStream_t st);
 
 // Post mix.
 hipError_t launch_post(const float* x, const float* f, const float* post, const float* comb,

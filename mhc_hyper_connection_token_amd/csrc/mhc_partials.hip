@@ -95,21 +95,22 @@ __global__ __launch_bounds__(256) void small_partials_long_kernel(const float* _
   }
 }
 
-int small_rows_per_thread(int S) {
-  const int rows = (2 + S) * S + 1;  // R rows and the sum of squares
-  const int rpt = (rows + 7) / 8;
+// Rows per thread for R weight rows and the sum of squares over 8 row slots.
+static int rows_per_thread(int R) {
+  const int rpt = (R + 1 + 7) / 8;
   return rpt <= 1 ? 1 : (rpt <= 2 ? 2 : (rpt <= 4 ? 4 : 0));
 }
 
-hipError_t launch_small_partials(const float* x, const float* fn_w, int T, int S, int H, int G,
-                                 int chunks_per_range, float* part, hipStream_t st) {
-  if (T < 1 || G < 1) return hipErrorInvalidValue;
-  const int n = S * H, R = (2 + S) * S;
+int small_rows_per_thread(int S) { return rows_per_thread((2 + S) * S); }
+
+hipError_t launch_small_partials_rows(const float* x, const float* fn_w, int T, int n, int R,
+                                      int G, int chunks_per_range, float* part, hipStream_t st) {
+  if (T < 1 || G < 1 || R < 1) return hipErrorInvalidValue;
   const int groups = (T + kSmallGroup - 1) / kSmallGroup;
   const int ymax = kSmallBlocks / G > 1 ? kSmallBlocks / G : 1;
   const dim3 grid(G, groups < ymax ? groups : ymax);
   const int ql = (chunks_per_range * 4 + 31) / 32;  // column quads per lane
-  const int rpt = small_rows_per_thread(S);
+  const int rpt = rows_per_thread(R);
 #define MHC_SP(RP_, QL_)                                                                       \
   if (rpt == RP_ && ql <= QL_) {                                                               \
     hipLaunchKernelGGL((small_partials_kernel<RP_, QL_>), grid, dim3(256), 0, st, x, fn_w, T, n, \
@@ -129,6 +130,12 @@ hipError_t launch_small_partials(const float* x, const float* fn_w, int T, int S
   MHC_SL(1) MHC_SL(2) MHC_SL(4)
 #undef MHC_SL
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_small_partials(const float* x, const float* fn_w, int T, int S, int H, int G,
+                                 int chunks_per_range, float* part, hipStream_t st) {
+  return launch_small_partials_rows(x, fn_w, T, S * H, (2 + S) * S, G, chunks_per_range, part,
+                                    st);
 }
 
 hipError_t launch_partials(const float* x, const float* fn_w, int T, int n, int R, int ntt,

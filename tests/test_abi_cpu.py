@@ -219,3 +219,32 @@ def test_ws_calls_refuse_before_any_gpu_work(lib):
     ws.cur = 0
     # T = 0 is a no-op that leaves the state slot alone
     assert lib.mhc_ws_site_post(ctypes.byref(ws), w, 0, None) == OK and ws.cur == 0
+
+
+# ------------------------------------------------------------------ trunk ends (host side)
+def test_trunk_calls_refuse_before_any_gpu_work(lib):
+    a, b = 1 << 30, 1 << 31
+    assert lib.mhc_expand(a, 4, 9, 128, b, None) == EUNSUP
+    assert lib.mhc_expand(a, 4, 4, 130, b, None) == EALIGN
+    assert lib.mhc_expand(None, 4, 4, 128, b, None) == EINVAL
+    assert lib.mhc_expand(a + 4, 4, 4, 128, b, None) == EALIGN
+    assert lib.mhc_expand(a, 4, 4, 128, a, None) == EOVERLAP
+    assert lib.mhc_expand(None, 0, 4, 128, None, None) == OK
+    assert lib.mhc_mean(a, -1, 4, 128, b, None) == EINVAL
+    assert lib.mhc_mean(a, 4, 4, 128, a + 256, None) == EOVERLAP
+    assert lib.mhc_mean(a, 4, 4, 128, None, None) == EINVAL
+
+
+def test_head_check(lib):
+    T, S, H = 8, 4, 4096
+    base_addr = 1 << 30
+    x, w, sc, b, g, y = (base_addr + i * (1 << 26) for i in range(6))
+    assert mhc.head_check(x, w, sc, b, T, S, H, 1e-6, g, y) == OK
+    assert mhc.head_check(x, w, sc, b, T, S, H, 0.0, g, y) == EINVAL
+    assert mhc.head_check(x, w, sc, b, T, S, H, float("nan"), g, y) == EINVAL
+    assert mhc.head_check(x, w, sc, b, T, 9, H, 1e-6, g, y) == EUNSUP
+    assert mhc.head_check(x, w, 0, b, T, S, H, 1e-6, g, y) == EINVAL
+    assert mhc.head_check(x, w, sc + 4, b, T, S, H, 1e-6, g, y) == EALIGN
+    assert mhc.head_check(x, w, sc, b, T, S, H, 1e-6, x, y) == EOVERLAP
+    assert mhc.head_check(x, w, sc, b, T, S, H, 1e-6, g, g) == EOVERLAP
+    assert mhc.head_check(0, 0, 0, 0, 0, S, H, 1e-6, 0, 0) == OK
