@@ -41,8 +41,7 @@ def kernel_source_hash(names):
 # kernel -> the source files whose change invalidates its measured traffic
 KERNEL_SOURCES = {
     "post_kernel": ["mhc_post.hip", "mhc_device.h"],
-    "pre_call": ["mhc_fused.hip", "mhc_partials.hip", "mhc_finish.hip", "mhc_decode.hip",
-                 "mhc_split.h", "mhc_device.h", "mhc_api.hip"],
+    "pre_call": ["mhc_fused.hip", "mhc_device.h"],
 }
 
 
@@ -204,6 +203,113 @@ def alloc_zq8(T, S, H, torch):
             e(T, H // 32))
 
 
+def time_graph(torch, fn, calls=20, reps=5):
+    """Device µs per call: `calls` calls captured in a HIP graph on a side
+    stream, replayed `reps` times (HIP events around the replays)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(calls):
+            fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        g.replay()
+        a.record(s)
+        for _ in range(reps):
+            g.replay()
+        b.record(s)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (calls * reps)
+
+
+def time_ws_decode(mhc, torch, td, cd, sites=50, reps=20):
+    """Decode sites through a persistent workspace: a HIP graph of `sites` sites
+    (pre + post, the state ping-ponging between the workspace's two slots),
+    replayed; µs per site."""
+    ws = mhc.Workspace(cd.T, cd.S, cd.H)
+    ws.state[:cd.T].copy_(td["x"])
+
+    def walk():
+        for _ in range(sites):
+            ws.site_pre(td["fn_w"], td["scale"], td["base"], cd.iters, cd.eps, T=cd.T)
+            ws.site_post(td["f"], T=cd.T)
+    return time_graph(torch, walk, calls=1, reps=reps) / sites
+
+
+def time_walk(mhc, torch, c, x0, L, steps, warmup):
+    """A walk over L sites of the prefill chunk (each site its own synthetic
+    weights and branch output f, drawn on the device): (a) separate pre and post
+    calls per site, (b) the post half of each site fused with the next site's pre
+    (mhc_site_post_pre).  Returns (separate_us, fused_us) per site."""
+    T, S, H = c.T, c.S, c.H
+    R = (2 + S) * S
+    g = torch.Generator(device="cuda").manual_seed(7)
+    sites = []
+    for _ in range(L):
+        sites.append({
+            "fn_w": torch.randn((R, S * H), device="cuda", generator=g) / (S * H) ** 0.5,
+            "scale": torch.rand(3, device="cuda", generator=g) + 0.5,
+            "base": torch.randn(R, device="cuda", generator=g) * 0.1 ** 0.5,
+            "f": torch.rand((T, H), device="cuda", generator=g) * 2 - 1})
+    e = lambda *s: torch.empty(s, device="cuda", dtype=torch.float32)  # noqa: E731
+    xs = [x0, e(T, S, H), e(T, S, H)]
+    gates = [(e(T, S), e(T, S), e(T, S, S), e(T, H)) for _ in range(2)]
+
+    def separate():
+        x = xs[0]
+        for k, st in enumerate(sites):
+            o = gates[k % 2]
+            mhc.site_pre(x, st["fn_w"], st["scale"], st["base"], c.iters, c.eps, out=o)
+            xn = xs[1 + k % 2]
+            mhc.site_post(x, st["f"], o[1], o[2], out=xn)
+            x = xn
+
+    def fused():
+        o = gates[0]
+        mhc.site_pre(xs[0], sites[0]["fn_w"], sites[0]["scale"], sites[0]["base"], c.iters,
+                     c.eps, out=o)
+        x = xs[0]
+        for k in range(1, L):
+            st, prev = sites[k], sites[k - 1]
+            on = gates[k % 2]
+            xn = xs[1 + k % 2]
+            mhc.site_post_pre(x, prev["f"], o[1], o[2], st["fn_w"], st["scale"], st["base"],
+                              c.iters, c.eps, out=(xn,) + tuple(on))
+            x, o = xn, on
+        mhc.site_post(x, sites[-1]["f"], o[1], o[2], out=xs[1 + L % 2])
+
+    return (time_calls(torch, separate, steps, warmup) / L,
+            time_calls(torch, fused, steps, warmup) / L)
+
+
+def run_sweep(mhc, torch):
+    """Device time of the pre call, plain and decode-exact, over T (one JSON line
+    per shape)."""
+    from mhc_inputs import make_random_shape
+    for (S, H) in [(4, 4096), (2, 4096), (8, 7168)]:
+        for T in (1, 2, 4, 16, 17, 32, 64, 96, 128, 192, 256, 384, 512, 1024, 2048, 4096):
+            if S == 8 and T > 1024:
+                continue
+            t = to_dev(make_random_shape(T, S, H, seed=T), torch)
+            out, _ = alloc_out(T, S, H, torch)
+            res = {}
+            for name, exact in (("plain_us", False), ("exact_us", True)):
+                res[name] = round(time_graph(torch, lambda: mhc.site_pre(
+                    t["x"], t["fn_w"], t["scale"], t["base"], 20, 1e-6, out=out,
+                    exact=exact)), 2)
+            print(json.dumps({"sweep": "pre", "T": T, "streams": S, "hidden": H, **res}),
+                  flush=True)
+            del t, out
+            torch.cuda.empty_cache()
+
+
 def cpu_baseline(c, d, cpu_seconds=15.0, max_wall=30.0):
     """The fp64 oracle (pre + post) on the host cores over a bounded sample of the
     prefill workload: whole passes over its tokens (or a prefix, if one pass would
@@ -319,6 +425,8 @@ def main():
     ap.add_argument("--kernels-only", type=int, default=0)
     ap.add_argument("--workloads", default="prefill,decode",
                     help="configs (mhc_inputs.CONFIGS names) run by --kernels-only")
+    ap.add_argument("--sweep", action="store_true",
+                    help="print device time of the pre call (plain and decode-exact) over T")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="write the measured traffic file from two rocprofv3 counter runs")
     args = ap.parse_args()
@@ -341,6 +449,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     mhc.load_library()
+    if args.sweep:
+        run_sweep(mhc, torch)
+        return
     if args.kernels_only:
         run_kernels_only(args.kernels_only, mhc, torch, CONFIGS, make_site,
                          tuple(w for w in args.workloads.split(",") if w))
@@ -372,6 +483,7 @@ def main():
     dpre, dx = alloc_out(cd.T, cd.S, cd.H, torch)
     n = args.decode_sites
     d_eager_us, d_graph_us = time_decode(mhc, torch, td, cd, dpre, dx, n)
+    d_ws_us = time_ws_decode(mhc, torch, td, cd)
     pre1, post1 = algorithmic_bytes(cd.T, cd.S, cd.H)
 
     # ---- branch-input epilogue (RMS norm of y with a weight, q8 codes): the pre
@@ -387,6 +499,41 @@ def main():
                                                zq8=(nw_d, norm_eps, o7d))
     epi_b = zq8_bytes(c.T, c.H)
     epi_us = zq_pre_us - pre_ms * 1e3
+
+    # ---- a walk over 8 sites: separate calls against the fused post-then-pre schedule
+    walk_sep_us, walk_fused_us = time_walk(mhc, torch, c, t["x"], 8, max(3, args.steps // 5),
+                                           2)
+    walk = {"sites": 8,
+            "separate_us_per_site": round(walk_sep_us, 2),
+            "fused_us_per_site": round(walk_fused_us, 2),
+            "fused_tokens_per_s": round(c.T / (walk_fused_us * 1e-6), 1),
+            "fused_algorithmic_GBps": round((pre_b + post_b) / (walk_fused_us * 1e-6) / 1e9, 1),
+            "note": "prefill chunk, 8 sites with their own weights; fused: each site's post "
+                    "and the next site's pre in one kernel (mhc_site_post_pre), bit-identical "
+                    "to the separate calls; per-site bytes counted as for one pre + post"}
+
+    # ---- trunk entry and exit at the prefill size
+    emb = torch.empty((c.T, c.H), device="cuda", dtype=torch.float32).uniform_(-1, 1)
+    xs = torch.empty((c.T, c.S, c.H), device="cuda", dtype=torch.float32)
+    ym = torch.empty((c.T, c.H), device="cuda", dtype=torch.float32)
+    hw = t["fn_w"][:c.S].contiguous()
+    hs, hb = t["scale"][:1].contiguous(), t["base"][:c.S].contiguous()
+    hg = torch.empty((c.T, c.S), device="cuda", dtype=torch.float32)
+    exp_us = time_calls(torch, lambda: mhc.expand(emb, c.S, out=xs), args.steps, args.warmup)
+    mean_us = time_calls(torch, lambda: mhc.mean(t["x"], out=ym), args.steps, args.warmup)
+    head_us = time_calls(torch, lambda: mhc.head(t["x"], hw, hs, hb, c.eps, out=(hg, ym)),
+                         args.steps, args.warmup)
+    stream_b = 4 * c.T * c.H * (c.S + 1)  # expand and mean: T*H in, T*S*H out (or back)
+    head_b = 4 * (c.T * c.S * c.H + c.S * c.S * c.H + 1 + c.S + c.T * c.S + c.T * c.H)
+    trunk = {"expand_us": round(exp_us, 2), "mean_us": round(mean_us, 2),
+             "head_us": round(head_us, 2),
+             "expand_GBps": round(stream_b / (exp_us * 1e-6) / 1e9, 1),
+             "mean_GBps": round(stream_b / (mean_us * 1e-6) / 1e9, 1),
+             "head_algorithmic_GBps": round(head_b / (head_us * 1e-6) / 1e9, 1),
+             "note": "trunk entry (expand), unweighted exit (mean) and gated-head exit at "
+                     "T=4096 S=4 H=4096; HIP events per call; bytes count each operand once "
+                     "(the head's split path reads x twice)"}
+    del emb, xs, hg
 
     # ---- decode-exact batching: a 64-token verify batch and the prefill chunk
     from mhc_inputs import make_random_shape
@@ -426,11 +573,13 @@ def main():
                      "pre_us": round(pre_ms * 1e3, 2), "post_us": round(post_ms * 1e3, 2),
                      "algorithmic_bytes_per_step": pre_b + post_b},
         "decode_t1": {"us_per_site": round(d_graph_us, 3), "eager_us_per_site": round(d_eager_us, 3),
+                      "workspace_graph_us_per_site": round(d_ws_us, 3),
                       "sites": n,
                       "note": "us_per_site: a HIP graph of 50 sites (pre + post) replayed on one "
                               "stream, HIP-event time / sites (device time plus the gaps between "
                               "kernels); eager: the same sites as plain calls, host launch "
-                              "included",
+                              "included; workspace: 50 sites through a persistent workspace "
+                              "(ping-pong state), one graph",
                       "algorithmic_bytes_per_site": pre1 + post1},
         "epilogue_zq8": {
             "prefill_pre_zq8_us": round(zq_pre_us, 2),
@@ -441,6 +590,8 @@ def main():
             "note": "the pre call with the epilogue (z = RMS-norm(y) * nw, q8 codes and "
                     "scales); added_us = its time minus pre_us; decode sites as in decode_t1 "
                     "with the epilogue in the pre call"},
+        "site_walk": walk,
+        "trunk_ends": trunk,
         "pre_exact": dict(ex, note="mhc_site_pre_exact (every row bit-identical to a solo "
                                      "T=1 call) against mhc_site_pre, same inputs, S=4 H=4096"),
         "roofline": roofline,

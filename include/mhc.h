@@ -150,6 +150,40 @@ int mhc_site_pre_zq8(const float* x, const float* fn_w, const float* scale, cons
                      signed char* q, float* d, void* stream);
 
 /*
+ * mhc_site_post_pre -- the post half of one site followed by the pre half of the
+ * next site on its output, the order in which a trunk runs them (hyper.rs page,
+ * module doc: per site, attention then MLP, each site's output state is the
+ * next site's input).  Equivalent to
+ *     mhc_site_post(x, f, post_in, comb_in, ..., x_out);
+ *     mhc_site_pre(x_out, fn_w, scale, base, ..., pre, post, comb, y);
+ * and bit-identical to that pair.  Where the token-tiled pre kernel serves the
+ * shape (S <= 4, T >= 256) one kernel does both and the new state is not read
+ * back from memory.  The _zq8 form adds the branch-input epilogue of the second
+ * site, as mhc_site_pre_zq8.
+ *
+ * Arguments: x, f, post_in, comb_in as mhc_site_post (the first site);
+ * fn_w, scale, base, iters, eps as mhc_site_pre (the second site); x_out is the
+ * first site's output and the second site's input; pre, post, comb, y (and
+ * z, q, d) the second site's outputs.  An output that overlaps an input or
+ * another output is MHC_EOVERLAP (a walk alternates two sets of gate buffers).
+ */
+int mhc_site_post_pre(const float* x, const float* f, const float* post_in, const float* comb_in,
+                      const float* fn_w, const float* scale, const float* base, int T,
+                      int streams, int hidden, int iters, float eps, float* x_out, float* pre,
+                      float* post, float* comb, float* y, void* stream);
+int mhc_site_post_pre_zq8(const float* x, const float* f, const float* post_in,
+                          const float* comb_in, const float* fn_w, const float* scale,
+                          const float* base, const float* nw, int T, int streams, int hidden,
+                          int iters, float eps, float norm_eps, float* x_out, float* pre,
+                          float* post, float* comb, float* y, float* z, signed char* q, float* d,
+                          void* stream);
+int mhc_site_post_pre_check(const float* x, const float* f, const float* post_in,
+                            const float* comb_in, const float* fn_w, const float* scale,
+                            const float* base, int T, int streams, int hidden, int iters,
+                            float eps, const float* x_out, const float* pre, const float* post,
+                            const float* comb, const float* y);
+
+/*
  * Trunk entry and exit (hyper.rs page: doc comments of `expand`,
  * `contract_mean` and `collapse`; the HyperHead loader sizes the head).
  *

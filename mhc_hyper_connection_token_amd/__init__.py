@@ -18,7 +18,8 @@ import ctypes
 import os
 
 __all__ = ["site_pre", "site_post", "site_pre_zq8", "site_pre_check", "site_post_check",
-           "site_pre_zq8_check", "expand", "mean", "head", "head_check", "Workspace",
+           "site_pre_zq8_check", "site_post_pre", "site_post_pre_check", "expand", "mean",
+           "head", "head_check", "Workspace",
            "workspace_bytes", "load_library", "MhcError", "LIB_PATH", "EXPORTED_SYMBOLS",
            "STATUS"]
 
@@ -30,6 +31,7 @@ EXPORTED_SYMBOLS = ("mhc_site_pre", "mhc_site_post", "mhc_site_pre_exact", "mhc_
                     "mhc_workspace_bytes", "mhc_workspace_struct_bytes", "mhc_workspace_init",
                     "mhc_ws_site_pre", "mhc_ws_site_pre_zq8", "mhc_ws_site_post",
                     "mhc_expand", "mhc_mean", "mhc_head", "mhc_head_check",
+                    "mhc_site_post_pre", "mhc_site_post_pre_zq8", "mhc_site_post_pre_check",
                     "mhc_status_string")
 
 STATUS = {0: "MHC_OK", 1: "MHC_EINVAL", 2: "MHC_EALIGN", 3: "MHC_EUNSUPPORTED",
@@ -85,6 +87,15 @@ def load_library() -> ctypes.CDLL:
     lib.mhc_ws_site_pre_zq8.restype = i
     lib.mhc_ws_site_post.argtypes = [wsp, vp, i, vp]
     lib.mhc_ws_site_post.restype = i
+    lib.mhc_site_post_pre.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, fl, vp, vp, vp,
+                                      vp, vp, vp]
+    lib.mhc_site_post_pre.restype = i
+    lib.mhc_site_post_pre_zq8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, fl, fl,
+                                          vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.mhc_site_post_pre_zq8.restype = i
+    lib.mhc_site_post_pre_check.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, fl, vp, vp,
+                                            vp, vp, vp]
+    lib.mhc_site_post_pre_check.restype = i
     lib.mhc_expand.argtypes = [vp, i, i, i, vp, vp]
     lib.mhc_expand.restype = i
     lib.mhc_mean.argtypes = [vp, i, i, i, vp, vp]
@@ -233,6 +244,61 @@ def site_pre_zq8_check(x_ptr, fn_w_ptr, scale_ptr, base_ptr, nw_ptr, T, S, H, it
     return lib.mhc_site_pre_zq8_check(x_ptr, fn_w_ptr, scale_ptr, base_ptr, nw_ptr, T, S, H,
                                       iters, float(eps), float(norm_eps), pre_ptr, post_ptr,
                                       comb_ptr, y_ptr, z_ptr, q_ptr, d_ptr)
+
+
+def site_post_pre(x, f, post, comb, fn_w, scale, base, iters: int, eps: float, *, nw=None,
+                  norm_eps: float = 1e-5, out=None, stream=None):
+    """The post half of a site (x, f, post, comb) followed by the pre half of the
+    next site (fn_w, scale, base) on its output.  Returns (x_out, pre, post, comb, y),
+    plus (z, q, d) when the norm weight nw of the next site's epilogue is given;
+    `out` may supply that tuple."""
+    import torch
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be [T, S, H]")
+    T, S, H = x.shape
+    R = (2 + S) * S
+    px = _dev(x, "x")
+    pf = _dev(f, "f", (T, H))
+    ppi = _dev(post, "post", (T, S))
+    pci = _dev(comb, "comb", (T, S, S))
+    pw = _dev(fn_w, "fn_w", (R, S * H))
+    ps = _dev(scale, "scale", (3,))
+    pb = _dev(base, "base", (R,))
+    if out is None:
+        e = lambda s, dt=torch.float32: torch.empty(s, device=x.device, dtype=dt)  # noqa: E731
+        out = (e((T, S, H)), e((T, S)), e((T, S)), e((T, S, S)), e((T, H)))
+        if nw is not None:
+            out = out + (e((T, H)), e((T, H), torch.int8), e((T, H // 32)))
+    ptrs = [_dev(out[0], "x_out", (T, S, H)), _dev(out[1], "pre", (T, S)),
+            _dev(out[2], "post", (T, S)), _dev(out[3], "comb", (T, S, S)),
+            _dev(out[4], "y", (T, H))]
+    st = _stream_handle(stream)
+    if nw is None:
+        rc = lib.mhc_site_post_pre(px, pf, ppi, pci, pw, ps, pb, T, S, H, int(iters),
+                                   float(eps), *ptrs, st)
+        name = "mhc_site_post_pre"
+    else:
+        z, q, d = out[5], out[6], out[7]
+        if q.dtype != torch.int8 or not q.is_cuda or not q.is_contiguous():
+            raise ValueError("q must be a contiguous int8 GPU tensor")
+        rc = lib.mhc_site_post_pre_zq8(px, pf, ppi, pci, pw, ps, pb, _dev(nw, "nw", (H,)), T, S,
+                                       H, int(iters), float(eps), float(norm_eps), *ptrs,
+                                       _dev(z, "z", (T, H)), q.data_ptr(),
+                                       _dev(d, "d", (T, H // 32)), st)
+        name = "mhc_site_post_pre_zq8"
+    if rc != 0:
+        raise MhcError(name, rc, _status_text(lib, rc))
+    return out
+
+
+def site_post_pre_check(x_ptr, f_ptr, post_ptr, comb_ptr, fn_w_ptr, scale_ptr, base_ptr, T, S,
+                        H, iters, eps, x_out_ptr, pre2_ptr, post2_ptr, comb2_ptr, y2_ptr) -> int:
+    """The library's host-side argument check of mhc_site_post_pre on raw addresses."""
+    lib = load_library()
+    return lib.mhc_site_post_pre_check(x_ptr, f_ptr, post_ptr, comb_ptr, fn_w_ptr, scale_ptr,
+                                       base_ptr, T, S, H, iters, float(eps), x_out_ptr, pre2_ptr,
+                                       post2_ptr, comb2_ptr, y2_ptr)
 
 
 def expand(e, streams: int, *, out=None, stream=None):

@@ -233,7 +233,7 @@ int site_pre_run(const float* x, const float* fn_w, const float* scale, const fl
     Scratch sc;
     if ((rc = acquire_scratch(src, mhc::fused_pack_bytes(S, H), &sc))) return rc;
     if (mhc::launch_fused_pre(x, fn_w, scale, base, T, S, H, iters, eps, pre, post, comb, y,
-                              sc.general, zq, st) != hipSuccess)
+                              sc.general, zq, nullptr, st) != hipSuccess)
       return MHC_EHIP;
     zq_done = true;
   } else {
@@ -263,6 +263,28 @@ int site_pre_run(const float* x, const float* fn_w, const float* scale, const fl
       mhc::launch_zq8(y, zq->nw, T, H, zq->norm_eps, zq->z, zq->q, zq->d, st) != hipSuccess)
     return MHC_EHIP;
   return MHC_OK;
+}
+
+// The post half of one site followed by the pre half of the next on its output.
+// Where the fused kernel serves the shape, one launch (plus the weight pack)
+// does both and the new state is never read back; elsewhere the post kernel
+// and then the pre chain.
+int site_post_pre_run(const float* x, const float* f, const float* post_in, const float* comb_in,
+                      const float* fn_w, const float* scale, const float* base, int T, int S,
+                      int H, int iters, float eps, float* x_out, float* pre, float* post,
+                      float* comb, float* y, const mhc::Zq8Out* zq, hipStream_t st) {
+  if (T >= kFusedMinTokens && mhc::fused_supported(S, H)) {
+    Scratch sc;
+    int rc;
+    if ((rc = get_scratch(mhc::fused_pack_bytes(S, H), &sc))) return rc;
+    const mhc::PostIn pin{f, post_in, comb_in, x_out};
+    return mhc::launch_fused_pre(x, fn_w, scale, base, T, S, H, iters, eps, pre, post, comb, y,
+                                 sc.general, zq, &pin, st) == hipSuccess
+               ? MHC_OK
+               : MHC_EHIP;
+  }
+  if (mhc::launch_post(x, f, post_in, comb_in, T, S, H, x_out, st) != hipSuccess) return MHC_EHIP;
+  return site_pre_run(x_out, fn_w, scale, base, T, S, H, iters, eps, pre, post, comb, y, zq, st);
 }
 
 }  // namespace
@@ -361,6 +383,67 @@ int mhc_site_pre_zq8(const float* x, const float* fn_w, const float* scale, cons
   const mhc::Zq8Out zq{nw, norm_eps, z, q, d};
   return site_pre_run(x, fn_w, scale, base, T, streams, hidden, iters, eps, pre, post, comb, y,
                       &zq, static_cast<hipStream_t>(stream));
+}
+
+int mhc_site_post_pre_check(const float* x, const float* f, const float* post_in,
+                            const float* comb_in, const float* fn_w, const float* scale,
+                            const float* base, int T, int streams, int hidden, int iters,
+                            float eps, const float* x_out, const float* pre, const float* post,
+                            const float* comb, const float* y) {
+  int rc = mhc_site_post_check(x, f, post_in, comb_in, T, streams, hidden, x_out);
+  if (rc) return rc;
+  if ((rc = mhc_site_pre_check(x_out, fn_w, scale, base, T, streams, hidden, iters, eps, pre,
+                               post, comb, y)))
+    return rc;
+  if (T == 0) return MHC_OK;
+  // the next site's outputs against the previous site's inputs
+  const size_t S = streams, H = hidden, Tz = T;
+  const Span old_in[] = {span(x, Tz * S * H * 4), span(f, Tz * H * 4),
+                         span(post_in, Tz * S * 4), span(comb_in, Tz * S * S * 4)};
+  const Span out[] = {span(pre, Tz * S * 4), span(post, Tz * S * 4), span(comb, Tz * S * S * 4),
+                      span(y, Tz * H * 4)};
+  for (const Span& o : out)
+    for (const Span& i : old_in)
+      if (overlaps(o, i)) return MHC_EOVERLAP;
+  return MHC_OK;
+}
+
+int mhc_site_post_pre(const float* x, const float* f, const float* post_in, const float* comb_in,
+                      const float* fn_w, const float* scale, const float* base, int T,
+                      int streams, int hidden, int iters, float eps, float* x_out, float* pre,
+                      float* post, float* comb, float* y, void* stream) {
+  int rc = mhc_site_post_pre_check(x, f, post_in, comb_in, fn_w, scale, base, T, streams, hidden,
+                                   iters, eps, x_out, pre, post, comb, y);
+  if (rc || T == 0) return rc;
+  return site_post_pre_run(x, f, post_in, comb_in, fn_w, scale, base, T, streams, hidden, iters,
+                           eps, x_out, pre, post, comb, y, nullptr,
+                           static_cast<hipStream_t>(stream));
+}
+
+int mhc_site_post_pre_zq8(const float* x, const float* f, const float* post_in,
+                          const float* comb_in, const float* fn_w, const float* scale,
+                          const float* base, const float* nw, int T, int streams, int hidden,
+                          int iters, float eps, float norm_eps, float* x_out, float* pre,
+                          float* post, float* comb, float* y, float* z, signed char* q, float* d,
+                          void* stream) {
+  int rc = mhc_site_post_pre_check(x, f, post_in, comb_in, fn_w, scale, base, T, streams, hidden,
+                                   iters, eps, x_out, pre, post, comb, y);
+  if (rc) return rc;
+  if ((rc = mhc_site_pre_zq8_check(x_out, fn_w, scale, base, nw, T, streams, hidden, iters, eps,
+                                   norm_eps, pre, post, comb, y, z, q, d)))
+    return rc;
+  if (T == 0) return MHC_OK;
+  const size_t S = streams, H = hidden, Tz = T;
+  const Span old_in[] = {span(x, Tz * S * H * 4), span(f, Tz * H * 4),
+                         span(post_in, Tz * S * 4), span(comb_in, Tz * S * S * 4)};
+  const Span out[] = {span(z, Tz * H * 4), span(q, Tz * H), span(d, Tz * (H / 32) * 4)};
+  for (const Span& o : out)
+    for (const Span& i : old_in)
+      if (overlaps(o, i)) return MHC_EOVERLAP;
+  const mhc::Zq8Out zq{nw, norm_eps, z, q, d};
+  return site_post_pre_run(x, f, post_in, comb_in, fn_w, scale, base, T, streams, hidden, iters,
+                           eps, x_out, pre, post, comb, y, &zq,
+                           static_cast<hipStream_t>(stream));
 }
 
 int mhc_site_post(const float* x, const float* f, const float* post, const float* comb, int T,

@@ -245,6 +245,28 @@ __device__ __forceinline__ float4 collapse4(const float* pre, const float4* xs, 
   return o;
 }
 
+// The post mix of one hidden quad of target stream k (hyper.rs page, doc comment
+// of `post`): post_k * f + sum_j comb[j][k] * x_j, the first term a product and
+// the sources added in ascending order by fused multiply-adds.  comb[j][k] is
+// cj[j * cstride].  Shared by the post kernel and the fused post-then-pre
+// kernel, so both write the same bits.
+template <int SMAX>
+__device__ __forceinline__ float4 post_mix4(float pk, const float* cj, int cstride,
+                                            const float4* xv, float4 fv, int S) {
+  float4 o = make_float4(pk * fv.x, pk * fv.y, pk * fv.z, pk * fv.w);
+#pragma unroll
+  for (int j = 0; j < SMAX; ++j) {
+    if (j < S) {
+      const float c = cj[j * cstride];
+      o.x = fmaf(c, xv[j].x, o.x);
+      o.y = fmaf(c, xv[j].y, o.y);
+      o.z = fmaf(c, xv[j].z, o.z);
+      o.w = fmaf(c, xv[j].w, o.w);
+    }
+  }
+  return o;
+}
+
 // ---------------------------------------------------------------- branch-input epilogue
 // (hc_fused_gate.rs page, the v4z timing block: the norm and the q8 encoding of
 // the branch input.)  z = y * r * w per entry, r = 1/sqrt(mean y^2 + norm_eps);

@@ -22,6 +22,11 @@
 // With ZQ the tail also runs the branch-input epilogue (z = RMS-norm(y) * nw,
 // its q8 codes and scales) from the y still in registers: one more barrier for
 // the per-token sum of squares, and y is never read back.
+//
+// With POST the kernel first finishes the previous site: it reads that site's
+// input state, branch output and gates, computes the post mix in registers,
+// writes it out as the new state, and runs this site's pre chain on it, so the
+// new state is never read back from memory.
 #include "mhc_device.h"
 #include "mhc_kernels.h"
 
@@ -54,12 +59,12 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const float* __restric
                   : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-template <int S, int CPW, int WD, bool ZQ>
+template <int S, int CPW, int WD, bool ZQ, bool POST>
 __global__ __launch_bounds__(512) void fused_pre_kernel(
     const float* __restrict__ x, const float4* __restrict__ wpack,
     const float* __restrict__ scale, const float* __restrict__ base, int T, int H, int iters,
     float eps, float* __restrict__ pre, float* __restrict__ post, float* __restrict__ comb,
-    float* __restrict__ y, Zq8Out zq) {
+    float* __restrict__ y, Zq8Out zq, PostIn pin) {
   constexpr int R = (2 + S) * S;
   constexpr int RG = (R + 3) / 4;  // weight-row groups of 4
   constexpr int NW = 8;
@@ -70,8 +75,18 @@ __global__ __launch_bounds__(512) void fused_pre_kernel(
   __shared__ float pre_lds[4 * 8];
   __shared__ float params[3 + R];
   __shared__ float zred[ZQ ? NW : 1][4];
+  __shared__ float gpc[POST ? 4 : 1][POST ? S * (S + 1) : 1];  // post gates, then comb [j][k]
 
   stage_site_params(scale, base, R, params);
+  if constexpr (POST) {
+    // the previous site's gates of the tile's tokens (a barrier follows below)
+    constexpr int G1 = S * (S + 1);
+    for (int i = threadIdx.x; i < 4 * G1; i += 512) {
+      const int u = i / G1, e = i - u * G1;
+      const int tk = min((int)blockIdx.x * 4 + u, T - 1);
+      gpc[u][e] = e < S ? pin.post[(size_t)tk * S + e] : pin.comb[(size_t)tk * S * S + (e - S)];
+    }
+  }
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * 4;
@@ -111,6 +126,33 @@ __global__ __launch_bounds__(512) void fused_pre_kernel(
   float ss = 0.f;
 #pragma unroll
   for (int ci = 0; ci < NCH; ++ci) load_x(ci);
+  if constexpr (POST) {
+    // The previous site's post mix, in registers: x' = post * f + comb^T x for
+    // every column block, written out as the next state and kept as this
+    // site's input.  A lane holds all S streams of its columns.
+    float4 fq[CPW];
+    const float* ft = pin.f + (size_t)(tok_ok ? tok : 0) * H;
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      const int h = 64 * (wave * CPW + u) + 4 * bq;
+      fq[u] = nt_load4(ft + (h < H ? h : 0));
+    }
+    __syncthreads();  // gpc staged
+    const float* g = &gpc[tq][0];
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) {
+      const int h = 64 * (wave * CPW + u) + 4 * bq;
+      float4 xs[S];
+#pragma unroll
+      for (int c = 0; c < S; ++c) xs[c] = xr[c * CPW + u];
+#pragma unroll
+      for (int k = 0; k < S; ++k) {
+        const float4 o = post_mix4<S>(g[k], g + S + k, S, xs, fq[u], S);
+        xr[k * CPW + u] = o;
+        if (tok_ok && h < H) nt_store4(pin.x_out + ((size_t)tok * S + k) * H + h, o);
+      }
+    }
+  }
 #pragma unroll
   for (int ci = 0; ci < WD && ci < NCH; ++ci) load_w(ci, wb[ci]);
 #pragma unroll
@@ -269,23 +311,32 @@ size_t fused_pack_bytes(int S, int H) {
 hipError_t launch_fused_pre(const float* x, const float* fn_w, const float* scale,
                             const float* base, int T, int S, int H, int iters, float eps,
                             float* pre, float* post, float* comb, float* y, float* wpack,
-                            const Zq8Out* zq, hipStream_t st) {
+                            const Zq8Out* zq, const PostIn* pin, hipStream_t st) {
   if (!fused_supported(S, H) || (zq && H % 32 != 0)) return hipErrorInvalidValue;
   const Zq8Out zv = zq ? *zq : Zq8Out{nullptr, 0.f, nullptr, nullptr, nullptr};
+  const PostIn pv = pin ? *pin : PostIn{nullptr, nullptr, nullptr, nullptr};
   const int cpw = fused_cpw(H);
   const int total = (int)(fused_pack_bytes(S, H) / sizeof(float4));
   float4* pk = reinterpret_cast<float4*>(wpack);
   dim3 grid((T + 3) / 4);
+#define MHC_FK(SS, CC, Z, P)                                                                  \
+  hipLaunchKernelGGL((fused_pre_kernel<SS, CC, 1, Z, P>), grid, dim3(512), 0, st, x, pk, scale, \
+                     base, T, H, iters, eps, pre, post, comb, y, zv, pv)
 #define MHC_FU(SS, CC)                                                                        \
   if (S == SS && cpw == CC) {                                                                 \
     hipLaunchKernelGGL((pack_weight_kernel<SS, CC>), dim3((total + 255) / 256), dim3(256), 0, \
                        st, fn_w, H, pk);                                                      \
-    if (zq)                                                                                   \
-      hipLaunchKernelGGL((fused_pre_kernel<SS, CC, 1, true>), grid, dim3(512), 0, st, x, pk,   \
-                         scale, base, T, H, iters, eps, pre, post, comb, y, zv);              \
-    else                                                                                      \
-      hipLaunchKernelGGL((fused_pre_kernel<SS, CC, 1, false>), grid, dim3(512), 0, st, x, pk,  \
-                         scale, base, T, H, iters, eps, pre, post, comb, y, zv);              \
+    if (pin) {                                                                                \
+      if (zq)                                                                                 \
+        MHC_FK(SS, CC, true, true);                                                           \
+      else                                                                                    \
+        MHC_FK(SS, CC, false, true);                                                          \
+    } else {                                                                                  \
+      if (zq)                                                                                 \
+        MHC_FK(SS, CC, true, false);                                                          \
+      else                                                                                    \
+        MHC_FK(SS, CC, false, false);                                                         \
+    }                                                                                         \
     return hipGetLastError();                                                                 \
   }
   MHC_FU(1, 1) MHC_FU(1, 2) MHC_FU(1, 4) MHC_FU(1, 8) MHC_FU(1, 16)
@@ -293,6 +344,7 @@ hipError_t launch_fused_pre(const float* x, const float* fn_w, const float* scal
   MHC_FU(3, 1) MHC_FU(3, 2) MHC_FU(3, 4) MHC_FU(3, 8)
   MHC_FU(4, 1) MHC_FU(4, 2) MHC_FU(4, 4) MHC_FU(4, 8)
 #undef MHC_FU
+#undef MHC_FK
   return hipErrorInvalidValue;
 }
 

@@ -33,16 +33,27 @@ hipError_t launch_finish(const float* x, const float* part, int G, int T, int S,
                          const float* scale, const float* base, int iters, float eps,
                          float* pre, float* post, float* comb, float* y, hipStream_t st);
 
+// The previous site's post half, run in front of a pre chain: its input state
+// x (the pre chain's x argument), branch output f [T][H] and gates post [T][S],
+// comb [T][S][S]; the post mix is written to x_out and feeds the pre chain.
+struct PostIn {
+  const float* f;
+  const float* post;
+  const float* comb;
+  float* x_out;
+};
+
 // Token-tiled fused pre chain (slab held on chip), for S <= 4 and H up to a
 // register budget; fused_supported() says whether a shape qualifies.
 // wpack: scratch of fused_pack_bytes(S, H) bytes for the weight in operand order.
-// With zq non-null (H % 32 == 0) the kernel also writes the branch-input epilogue.
+// With zq non-null (H % 32 == 0) the kernel also writes the branch-input epilogue;
+// with pin non-null it first runs the previous site's post mix on x.
 bool fused_supported(int S, int H);
 size_t fused_pack_bytes(int S, int H);
 hipError_t launch_fused_pre(const float* x, const float* fn_w, const float* scale,
                             const float* base, int T, int S, int H, int iters, float eps,
                             float* pre, float* post, float* comb, float* y, float* wpack,
-                            const Zq8Out* zq, hipStream_t st);
+                            const Zq8Out* zq, const PostIn* pin, hipStream_t st);
 
 // Single-launch pre chain and branch-input epilogue of one token (S <= 4,
 // H % 32 == 0; decode_zq8_supported): split-K partials into `part` (same G /

@@ -3,8 +3,9 @@
 //
 // A pure stream: every thread owns one hidden quad (16 bytes) of one token,
 // reads the S source quads and the branch quad once (non-temporal: they are
-// not read again by this kernel), and writes the S target quads once.  The token's gates are block-uniform (one token per block row),
-// so they come through scalar loads.  HBM-bound: the bytes per token are
+// not read again by this kernel), and writes the S target quads once.  The
+// token's gates are block-uniform (one token per block row), so they come
+// through scalar loads.  HBM-bound: the bytes per token are
 // 4*(2*S*H + H) plus the gates.
 #include "mhc_device.h"
 #include "mhc_kernels.h"
@@ -36,17 +37,7 @@ __global__ __launch_bounds__(256) void post_kernel(const float* __restrict__ x,
   const float4 fv = nt_load4(f + ((size_t)t * HQ + q) * 4);
   float4* ot = reinterpret_cast<float4*>(out) + (size_t)t * S * HQ + q;
 #pragma unroll
-  for (int k = 0; k < S; ++k) {
-    float4 o = make_float4(pk[k] * fv.x, pk[k] * fv.y, pk[k] * fv.z, pk[k] * fv.w);
-#pragma unroll
-    for (int j = 0; j < S; ++j) {
-      o.x = fmaf(ck[j][k], xv[j].x, o.x);
-      o.y = fmaf(ck[j][k], xv[j].y, o.y);
-      o.z = fmaf(ck[j][k], xv[j].z, o.z);
-      o.w = fmaf(ck[j][k], xv[j].w, o.w);
-    }
-    ot[(size_t)k * HQ] = o;
-  }
+  for (int k = 0; k < S; ++k) ot[(size_t)k * HQ] = post_mix4<S>(pk[k], &ck[0][k], S, xv, fv, S);
 }
 
 hipError_t launch_post(const float* x, const float* f, const float* post, const float* comb,

@@ -248,3 +248,25 @@ def test_head_check(lib):
     assert mhc.head_check(x, w, sc, b, T, S, H, 1e-6, x, y) == EOVERLAP
     assert mhc.head_check(x, w, sc, b, T, S, H, 1e-6, g, g) == EOVERLAP
     assert mhc.head_check(0, 0, 0, 0, 0, S, H, 1e-6, 0, 0) == OK
+
+
+def test_post_pre_check(lib):
+    T, S, H = 8, 4, 4096
+    a = [(1 << 30) + i * (1 << 26) for i in range(12)]
+    x, f, po, co, w, sc, b, xo, pre2, po2, co2, y2 = a
+    ok = mhc.site_post_pre_check(x, f, po, co, w, sc, b, T, S, H, 20, 1e-6, xo, pre2, po2, co2, y2)
+    assert ok == OK
+    # the new state over the old one, the new gates over the old gates: refused
+    assert mhc.site_post_pre_check(x, f, po, co, w, sc, b, T, S, H, 20, 1e-6, x, pre2, po2, co2,
+                                   y2) == EOVERLAP
+    assert mhc.site_post_pre_check(x, f, po, co, w, sc, b, T, S, H, 20, 1e-6, xo, pre2, po, co2,
+                                   y2) == EOVERLAP
+    assert mhc.site_post_pre_check(x, f, po, co, w, sc, b, T, S, H, 20, 1e-6, xo, pre2, po2, co2,
+                                   f) == EOVERLAP
+    # both halves' own checks apply
+    assert mhc.site_post_pre_check(x, f, po, co, w, sc, b, T, S, H, 0, 1e-6, xo, pre2, po2, co2,
+                                   y2) == EINVAL
+    assert mhc.site_post_pre_check(x, 0, po, co, w, sc, b, T, S, H, 20, 1e-6, xo, pre2, po2, co2,
+                                   y2) == EINVAL
+    assert mhc.site_post_pre_check(x, f, po, co, w, sc, b, T, 9, H, 20, 1e-6, xo, pre2, po2, co2,
+                                   y2) == EUNSUP
