@@ -42,6 +42,7 @@ def kernel_source_hash(names):
 KERNEL_SOURCES = {
     "post_kernel": ["mhc_post.hip", "mhc_device.h"],
     "pre_call": ["mhc_fused.hip", "mhc_device.h"],
+    "walk_call": ["mhc_fused.hip", "mhc_device.h"],
 }
 
 
@@ -63,7 +64,8 @@ def alloc_out(T, S, H, torch):
 
 def run_kernels_only(n, mhc, torch, CONFIGS, make_site, workloads=("prefill", "decode")):
     """A handful of launches of each workload kernel plus a plain 256 MiB device
-    copy (the reference for scaling rocprof's byte counters)."""
+    copy (the reference for scaling rocprof's byte counters).  With the prefill
+    workload it also runs n walk steps (a site's post fused with the next pre)."""
     for name in workloads:
         c = CONFIGS[name]
         t = to_dev(make_site(c), torch)
@@ -73,6 +75,13 @@ def run_kernels_only(n, mhc, torch, CONFIGS, make_site, workloads=("prefill", "d
             mhc.site_post(t["x"], t["f"], pre_o[1], pre_o[2], out=xo)
         torch.cuda.synchronize()
         print(f"[kernels-only] {name}: {n} sites", flush=True)
+        if name == "prefill":
+            nxt, _ = alloc_out(c.T, c.S, c.H, torch)
+            for _ in range(n):
+                mhc.site_post_pre(t["x"], t["f"], pre_o[1], pre_o[2], t["fn_w"], t["scale"],
+                                  t["base"], c.iters, c.eps, out=(xo,) + tuple(nxt))
+            torch.cuda.synchronize()
+            print(f"[kernels-only] {name}: {n} walk steps", flush=True)
     src = torch.empty(64 << 20, device="cuda", dtype=torch.float32)
     dst = torch.empty_like(src)
     for _ in range(n):
@@ -359,8 +368,9 @@ def load_traffic(kernel):
 
 # prefill kernels whose counters make up each measured unit
 TRAFFIC_UNITS = {
-    "pre_call": ["pack_weight_kernel", "fused_pre_kernel"],
-    "post_kernel": ["post_kernel"],
+    "pre_call": ["pack_weight_kernel<4, 8>", "fused_pre_kernel<4, 8, 1, false, false>"],
+    "post_kernel": ["post_kernel<4>"],
+    "walk_call": ["pack_weight_kernel<4, 8>", "fused_pre_kernel<4, 8, 1, false, true>"],
 }
 
 
@@ -379,7 +389,13 @@ def write_traffic(fetch_db, write_db):
         groups = defaultdict(list)
         for name, grid, cname, value in rows:
             if cname == counter:
-                short = name.split("(")[0].split("<")[0].split("::")[-1].strip()
+                # the kernel's name with its template arguments, without the
+                # return type, namespace and parameter list
+                head = name.split("(")[0].strip()
+                if head.startswith("void "):
+                    head = head[5:]
+                base, sep, targs = head.partition("<")
+                short = base.split("::")[-1].strip() + sep + targs
                 groups[(short, int(grid))].append(float(value))
         return {k: statistics.mean(v) for k, v in groups.items()}
 
@@ -503,14 +519,21 @@ def main():
     # ---- a walk over 8 sites: separate calls against the fused post-then-pre schedule
     walk_sep_us, walk_fused_us = time_walk(mhc, torch, c, t["x"], 8, max(3, args.steps // 5),
                                            2)
+    walk_traffic = load_traffic("walk_call")
     walk = {"sites": 8,
             "separate_us_per_site": round(walk_sep_us, 2),
             "fused_us_per_site": round(walk_fused_us, 2),
             "fused_tokens_per_s": round(c.T / (walk_fused_us * 1e-6), 1),
-            "fused_algorithmic_GBps": round((pre_b + post_b) / (walk_fused_us * 1e-6) / 1e9, 1),
+            "fused_equivalent_GBps": round((pre_b + post_b) / (walk_fused_us * 1e-6) / 1e9, 1),
+            "fused_call_traffic": walk_traffic,
+            "fused_traffic_GBps": (round(walk_traffic / (walk_fused_us * 1e-6) / 1e9, 1)
+                                   if walk_traffic else None),
             "note": "prefill chunk, 8 sites with their own weights; fused: each site's post "
                     "and the next site's pre in one kernel (mhc_site_post_pre), bit-identical "
-                    "to the separate calls; per-site bytes counted as for one pre + post"}
+                    "to the separate calls.  equivalent_GBps counts one pre + post's "
+                    "algorithmic bytes (the fused call does not re-read the new state); "
+                    "traffic_GBps is the measured HBM bytes of the fused call (pack + kernel) "
+                    "per site time"}
 
     # ---- trunk entry and exit at the prefill size
     emb = torch.empty((c.T, c.H), device="cuda", dtype=torch.float32).uniform_(-1, 1)

@@ -52,13 +52,15 @@ def test_write_traffic_scales_by_the_copy_kernel(tmp_path, monkeypatch):
         ("void mhc::pack_weight_kernel<4, 8>(float const*)", 98304, 800.0),
         ("void mhc::fused_pre_kernel<4, 8, 1, false, false>(...)", 524288, 100000.0),
         ("void mhc::fused_pre_kernel<4, 8, 1, false, false>(...)", 1024, 5.0),  # decode-size
-        ("void mhc::post_kernel<4>(...)", 4194304, 160000.0)])
+        ("void mhc::post_kernel<4>(...)", 4194304, 160000.0),
+        ("void mhc::fused_pre_kernel<4, 8, 1, false, true>(...)", 524288, 150000.0)])
     _counter_db(write, "WRITE_SIZE", [
         (copy, 1 << 20, 262144.0),
         ("void mhc::pack_weight_kernel<4, 8>(float const*)", 98304, 1536.0),
         ("void mhc::fused_pre_kernel<4, 8, 1, false, false>(...)", 524288, 60000.0),
         ("void mhc::fused_pre_kernel<4, 8, 1, false, false>(...)", 1024, 1.0),
-        ("void mhc::post_kernel<4>(...)", 4194304, 262144.0)])
+        ("void mhc::post_kernel<4>(...)", 4194304, 262144.0),
+        ("void mhc::fused_pre_kernel<4, 8, 1, false, true>(...)", 524288, 330000.0)])
     out = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
     bench.write_traffic(fetch, write)
@@ -67,6 +69,9 @@ def test_write_traffic_scales_by_the_copy_kernel(tmp_path, monkeypatch):
     # the largest grid of each kernel is the prefill launch
     assert rec["pre_call"]["bytes_per_launch"] == round((2 * 800 + 1536 + 2 * 100000 + 60000) * 1024)
     assert rec["post_kernel"]["bytes_per_launch"] == round((2 * 160000 + 262144) * 1024)
+    # the walk kernel is told apart from the plain one by its template arguments
+    assert rec["walk_call"]["bytes_per_launch"] == round((2 * 800 + 1536 + 2 * 150000 + 330000)
+                                                         * 1024)
     # the stored hash is that of the measured kernels' sources
     assert rec["pre_call"]["source_hash"] == bench.kernel_source_hash(bench.KERNEL_SOURCES["pre_call"])
 
