@@ -128,28 +128,32 @@ __global__ __launch_bounds__(512) void fused_pre_kernel(
   for (int ci = 0; ci < NCH; ++ci) load_x(ci);
   if constexpr (POST) {
     // The previous site's post mix, in registers: x' = post * f + comb^T x for
-    // every column block, written out as the next state and kept as this
-    // site's input.  A lane holds all S streams of its columns.
-    float4 fq[CPW];
+    // every column block, kept as this site's input (and written out as the new
+    // state after the MFMA loop: a wave's memory operations retire in order, so
+    // stores issued here would hold up every weight load behind them).  A lane
+    // holds all S streams of its columns.  f comes in batches of 4 to 8
+    // column blocks, which bounds its registers.
+    constexpr int FB = CPW < 8 ? CPW : (CPW < 16 ? 8 : 4);
     const float* ft = pin.f + (size_t)(tok_ok ? tok : 0) * H;
-#pragma unroll
-    for (int u = 0; u < CPW; ++u) {
-      const int h = 64 * (wave * CPW + u) + 4 * bq;
-      fq[u] = nt_load4(ft + (h < H ? h : 0));
-    }
     __syncthreads();  // gpc staged
     const float* g = &gpc[tq][0];
 #pragma unroll
-    for (int u = 0; u < CPW; ++u) {
-      const int h = 64 * (wave * CPW + u) + 4 * bq;
-      float4 xs[S];
+    for (int u0 = 0; u0 < CPW; u0 += FB) {
+      float4 fq[FB];
 #pragma unroll
-      for (int c = 0; c < S; ++c) xs[c] = xr[c * CPW + u];
+      for (int i = 0; i < FB; ++i) {
+        const int h = 64 * (wave * CPW + u0 + i) + 4 * bq;
+        fq[i] = nt_load4(ft + (h < H ? h : 0));
+      }
 #pragma unroll
-      for (int k = 0; k < S; ++k) {
-        const float4 o = post_mix4<S>(g[k], g + S + k, S, xs, fq[u], S);
-        xr[k * CPW + u] = o;
-        if (tok_ok && h < H) nt_store4(pin.x_out + ((size_t)tok * S + k) * H + h, o);
+      for (int i = 0; i < FB; ++i) {
+        const int u = u0 + i;
+        float4 xs[S];
+#pragma unroll
+        for (int c = 0; c < S; ++c) xs[c] = xr[c * CPW + u];
+#pragma unroll
+        for (int k = 0; k < S; ++k)
+          xr[k * CPW + u] = post_mix4<S>(g[k], g + S + k, S, xs, fq[i], S);
       }
     }
   }
@@ -189,6 +193,18 @@ __global__ __launch_bounds__(512) void fused_pre_kernel(
     for (int rg = 0; rg < RG; ++rg)
       acc[rg] = __builtin_amdgcn_mfma_f32_4x4x1f32(aw, w[rg].w, acc[rg], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
+  }
+
+  if constexpr (POST) {
+    // the new state, written while the partial sums are being reduced
+    if (tok_ok) {
+#pragma unroll
+      for (int ci = 0; ci < NCH; ++ci) {
+        const int c = ci / CPW, u = ci % CPW;
+        const int h = 64 * (wave * CPW + u) + 4 * bq;
+        if (h < H) nt_store4(pin.x_out + ((size_t)tok * S + c) * H + h, xr[ci]);
+      }
+    }
   }
 
   // ---- fixed-order reduction: the 16 MFMA blocks in registers (DPP / permlane),
