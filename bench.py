@@ -451,7 +451,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the mHC site program is token-parallel with "
-              "no cross-GPU exchange, and this build runs and reports a single GPU "
+              "no cross-GPU exchange, and this benchmark runs and reports a single GPU "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
