@@ -298,6 +298,45 @@ def time_walk(mhc, torch, c, x0, L, steps, warmup):
             time_calls(torch, fused, steps, warmup) / L)
 
 
+def time_decode_walk(mhc, torch, c, x0, L=50, zq8=False):
+    """Decode sites (T=1) chained as a trunk runs them, four distinct site weights
+    in rotation, in one HIP graph: the first pre, then mhc_site_post_pre per
+    site, then the last post; with zq8 every pre carries the branch-input
+    epilogue.  Returns µs per site (graph replay)."""
+    T, S, H = c.T, c.S, c.H
+    R = (2 + S) * S
+    g = torch.Generator(device="cuda").manual_seed(11)
+    sites = [{"fn_w": torch.randn((R, S * H), device="cuda", generator=g) / (S * H) ** 0.5,
+              "scale": torch.rand(3, device="cuda", generator=g) + 0.5,
+              "base": torch.randn(R, device="cuda", generator=g) * 0.1 ** 0.5,
+              "f": torch.rand((T, H), device="cuda", generator=g) * 2 - 1} for _ in range(4)]
+    nw = torch.rand(H, device="cuda", generator=g) + 0.5
+    e = lambda *s, dt=torch.float32: torch.empty(s, device="cuda", dtype=dt)  # noqa: E731
+    xs = [x0.clone(), e(T, S, H), e(T, S, H)]
+    outs = [(e(T, S), e(T, S), e(T, S, S), e(T, H), e(T, H), e(T, H, dt=torch.int8),
+             e(T, H // 32)) for _ in range(2)]
+
+    def walk():
+        st = sites[0]
+        o = outs[0]
+        if zq8:
+            mhc.site_pre_zq8(xs[0], st["fn_w"], st["scale"], st["base"], nw, c.iters, c.eps,
+                             out=o)
+        else:
+            mhc.site_pre(xs[0], st["fn_w"], st["scale"], st["base"], c.iters, c.eps, out=o[:4])
+        x = xs[0]
+        for k in range(1, L):
+            st, prev = sites[k % 4], sites[(k - 1) % 4]
+            on = outs[k % 2]
+            xn = xs[1 + k % 2]
+            mhc.site_post_pre(x, prev["f"], o[1], o[2], st["fn_w"], st["scale"], st["base"],
+                              c.iters, c.eps, nw=nw if zq8 else None,
+                              out=(xn,) + tuple(on if zq8 else on[:4]))
+            x, o = xn, on
+        mhc.site_post(x, sites[(L - 1) % 4]["f"], o[1], o[2], out=xs[1 + L % 2])
+    return time_graph(torch, walk, calls=1, reps=20) / L
+
+
 def run_sweep(mhc, torch):
     """Device time of the pre call, plain and decode-exact, over T (one JSON line
     per shape)."""
@@ -500,6 +539,8 @@ def main():
     n = args.decode_sites
     d_eager_us, d_graph_us = time_decode(mhc, torch, td, cd, dpre, dx, n)
     d_ws_us = time_ws_decode(mhc, torch, td, cd)
+    d_walk_us = time_decode_walk(mhc, torch, cd, td["x"])
+    d_walk_zq_us = time_decode_walk(mhc, torch, cd, td["x"], zq8=True)
     pre1, post1 = algorithmic_bytes(cd.T, cd.S, cd.H)
 
     # ---- branch-input epilogue (RMS norm of y with a weight, q8 codes): the pre
@@ -597,12 +638,17 @@ def main():
                      "algorithmic_bytes_per_step": pre_b + post_b},
         "decode_t1": {"us_per_site": round(d_graph_us, 3), "eager_us_per_site": round(d_eager_us, 3),
                       "workspace_graph_us_per_site": round(d_ws_us, 3),
+                      "walk_graph_us_per_site": round(d_walk_us, 3),
+                      "walk_zq8_graph_us_per_site": round(d_walk_zq_us, 3),
                       "sites": n,
                       "note": "us_per_site: a HIP graph of 50 sites (pre + post) replayed on one "
                               "stream, HIP-event time / sites (device time plus the gaps between "
                               "kernels); eager: the same sites as plain calls, host launch "
                               "included; workspace: 50 sites through a persistent workspace "
-                              "(ping-pong state), one graph",
+                              "(ping-pong state), one graph; walk: 50 sites with four "
+                              "rotating weights chained with mhc_site_post_pre (at T=1 its "
+                              "post and pre run as separate kernels), one graph, without and "
+                              "with the epilogue",
                       "algorithmic_bytes_per_site": pre1 + post1},
         "epilogue_zq8": {
             "prefill_pre_zq8_us": round(zq_pre_us, 2),

@@ -1,8 +1,7 @@
 """A walk over sites with mhc_site_post_pre (the post half of a site fused with
 the pre half of the next) must be bit-identical to the same walk with separate
 mhc_site_pre / mhc_site_post calls, and every site within the oracle's
-tolerances.  Covers the one-kernel shapes (S <= 4, T >= 256) and the fallback
-(post kernel, then the pre chain), with and without the branch-input epilogue."""
+tolerances, with and without the branch-input epilogue."""
 import numpy as np
 import pytest
 
@@ -68,10 +67,17 @@ def _walk_fused(mhc, x0, sites, nw):
     return x, outs
 
 
+# T >= 256, S <= 4: the fused pre kernel with the post prologue; every other
+# shape: the post kernel, then the pre chain (small-batch split, single-launch
+# decode kernel with the epilogue, MFMA split for S > 4).
 @pytest.mark.parametrize("T,S,H,zq", [(256, 4, 4096, False), (300, 4, 1024, False),
                                       (260, 2, 1056, True), (256, 4, 4096, True),
-                                      (64, 4, 1024, False), (3, 8, 512, False),
-                                      (1, 4, 4096, True), (257, 1, 8192, False)])
+                                      (1, 4, 4096, False), (2, 4, 4096, True),
+                                      (5, 2, 1056, False), (17, 3, 512, True),
+                                      (64, 4, 1024, False), (200, 4, 4096, False),
+                                      (3, 4, 16384, False), (2, 2, 65536, False),
+                                      (3, 8, 512, False), (1, 4, 4096, True),
+                                      (257, 1, 8192, False)])
 def test_fused_walk_equals_separate_calls(mhc, T, S, H, zq):
     print(f"[case] walk T{T} S{S} H{H} zq8={zq}", flush=True)
     L = 4
