@@ -129,7 +129,9 @@ PrePlan plan_pre(int T, int S, int H) {
   const int n = S * H, R = (2 + S) * S, nrt = (R + 15) / 16;
   const int nchunks = (n + 15) / 16;
   PrePlan p;
-  p.ntt = T <= 16 ? 1 : (nrt <= 3 ? 4 : 2);
+  // 64-token blocks where the grid stays at 512 blocks or more (every weight
+  // fetch then serves 64 tokens); 32-token blocks for 4-5 row tiles below that
+  p.ntt = T <= 16 ? 1 : ((nrt <= 3 || T >= 512) ? 4 : 2);
   const int tiles = (T + 16 * p.ntt - 1) / (16 * p.ntt);
   int G;
   if (tiles == 1) {

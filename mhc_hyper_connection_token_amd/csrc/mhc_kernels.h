@@ -15,7 +15,7 @@ struct Zq8Out {
 };
 
 // Split-K partial mixes + sums of squares: part[G][T][R+1].
-// ntt = token tiles of 16 per block (1, 2 or 4, depending on the row-tile count).
+// ntt = token tiles of 16 per block (1, 2 or 4, by the row-tile count and T).
 hipError_t launch_partials(const float* x, const float* fn_w, int T, int n, int R, int ntt,
                            int G, int chunks_per_range, float* part, hipStream_t st);
 

@@ -30,8 +30,7 @@ __global__ __launch_bounds__(256) void partials_kernel(const float* __restrict__
                                                        const float* __restrict__ fn_w, int T,
                                                        int n, int R, int chunks_per_range,
                                                        float* __restrict__ part) {
-  constexpr int kVals = NRT * NTT * 4 + NTT;
-  __shared__ float red[4 * kVals * kWave];
+  __shared__ float red[4 * block_slice<NRT, NTT>() * kWave];
   const int g = blockIdx.y;
   const int nchunks = (n + 15) >> 4;
   const int c_beg = g * chunks_per_range;
@@ -145,7 +144,7 @@ hipError_t launch_partials(const float* x, const float* fn_w, int T, int n, int 
   if (nrt == NR && ntt == NT)                                                              \
     return launch_partials_t<NR, NT>(x, fn_w, T, n, R, G, chunks_per_range, part, st);
   MHC_P(1, 1) MHC_P(1, 4) MHC_P(2, 1) MHC_P(2, 4) MHC_P(3, 1) MHC_P(3, 4)
-  MHC_P(4, 1) MHC_P(4, 2) MHC_P(5, 1) MHC_P(5, 2)
+  MHC_P(4, 1) MHC_P(4, 2) MHC_P(4, 4) MHC_P(5, 1) MHC_P(5, 2) MHC_P(5, 4)
 #undef MHC_P
   return hipErrorInvalidValue;
 }

@@ -13,7 +13,7 @@ namespace mhc {
 // squares; t is the token's index in the batch).
 // 256 threads = four waves; wave w takes chunks c_beg + w, c_beg + w + 4, ...;
 // the four wave partials are added in wave order through `red`
-// (4 * (NRT*NTT*4 + NTT) * 64 floats of LDS).
+// (4 * block_slice<NRT, NTT>() * 64 floats of LDS).
 //
 // The contraction runs on v_mfma_f32_16x16x4_f32 (fp32 operands, exact fp32
 // products, fp32 accumulation): A = weight rows (16 per tile), B = token slabs
@@ -36,12 +36,25 @@ __device__ __forceinline__ float load_partial(const float* p) {
   return *p;
 }
 
+// Values each lane of a wave hands to the cross-wave sum, and the number of
+// slices that sum is staged in (the caller's `red` holds 4 * block_slice * 64
+// floats).
+template <int NRT, int NTT>
+constexpr int block_vals() { return NRT * NTT * 4 + NTT; }
+template <int NRT, int NTT>
+constexpr int block_passes() { return block_vals<NRT, NTT>() > 48 ? 2 : 1; }
+template <int NRT, int NTT>
+constexpr int block_slice() {
+  return (block_vals<NRT, NTT>() + block_passes<NRT, NTT>() - 1) / block_passes<NRT, NTT>();
+}
+
 template <int NRT, int NTT, class Sink>
 __device__ __forceinline__ void block_partials(const float* __restrict__ x,
                                                const float* __restrict__ fn_w, int T, int n,
                                                int R, int tok0, int c_beg, int c_end,
                                                float* red, Sink sink) {
-  constexpr int kVals = NRT * NTT * 4 + NTT;  // per lane, per wave
+  constexpr int kVals = block_vals<NRT, NTT>();  // per lane, per wave
+  constexpr int kPasses = block_passes<NRT, NTT>();
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int RP = R + 1;
@@ -144,35 +157,48 @@ __device__ __forceinline__ void block_partials(const float* __restrict__ x,
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt) ss[tt] = swap32_sum(swap16_sum(ss[tt]));
 
-  // Stage the wave's partials, then add the four waves in fixed order.
-  {
-    int v = 0;
+  // Stage the wave's partials, then add the four waves in fixed order, in
+  // kPasses slices of the values (bounds the LDS; the order of every sum is the
+  // same for any slicing).
+  constexpr int kSlice = (kVals + kPasses - 1) / kPasses;
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int v0 = pass * kSlice;
+    {
+      int v = 0;
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt)
+      for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red[(wave * kVals + v++) * kWave + lane] = acc[rt][tt][e];
+        for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) red[(wave * kVals + v++) * kWave + lane] = ss[tt];
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < kVals * kWave; idx += 256) {
-    const int v = idx / kWave, l = idx % kWave;
-    const float s = ((red[(0 * kVals + v) * kWave + l] + red[(1 * kVals + v) * kWave + l]) +
-                     red[(2 * kVals + v) * kWave + l]) +
-                    red[(3 * kVals + v) * kWave + l];
-    if (v < NRT * NTT * 4) {
-      // MFMA D layout: row = 4*(l/16) + e within the row tile, token = l % 16.
-      const int rt = v / (NTT * 4), tt = (v / 4) % NTT, e = v % 4;
-      const int r = rt * 16 + 4 * (l >> 4) + e;
-      const int t = tok0 + tt * 16 + (l & 15);
-      if (r < R && t < T) sink((size_t)t * RP + r, s);
-    } else {
-      const int tt = v - NRT * NTT * 4;
-      const int t = tok0 + tt * 16 + (l & 15);
-      if (l < 16 && t < T) sink((size_t)t * RP + R, s);
+          for (int e = 0; e < 4; ++e, ++v)
+            if (v >= v0 && v < v0 + kSlice)
+              red[(wave * kSlice + v - v0) * kWave + lane] = acc[rt][tt][e];
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt, ++v)
+        if (v >= v0 && v < v0 + kSlice) red[(wave * kSlice + v - v0) * kWave + lane] = ss[tt];
     }
+    __syncthreads();
+    const int nv = kVals - v0 < kSlice ? kVals - v0 : kSlice;
+    for (int idx = threadIdx.x; idx < nv * kWave; idx += 256) {
+      const int vs = idx / kWave, l = idx % kWave;
+      const int v = v0 + vs;
+      const float s = ((red[(0 * kSlice + vs) * kWave + l] + red[(1 * kSlice + vs) * kWave + l]) +
+                       red[(2 * kSlice + vs) * kWave + l]) +
+                      red[(3 * kSlice + vs) * kWave + l];
+      if (v < NRT * NTT * 4) {
+        // MFMA D layout: row = 4*(l/16) + e within the row tile, token = l % 16.
+        const int rt = v / (NTT * 4), tt = (v / 4) % NTT, e = v % 4;
+        const int r = rt * 16 + 4 * (l >> 4) + e;
+        const int t = tok0 + tt * 16 + (l & 15);
+        if (r < R && t < T) sink((size_t)t * RP + r, s);
+      } else {
+        const int tt = v - NRT * NTT * 4;
+        const int t = tok0 + tt * 16 + (l & 15);
+        if (l < 16 && t < T) sink((size_t)t * RP + R, s);
+      }
+    }
+    if (pass + 1 < kPasses) __syncthreads();
   }
 }
 
