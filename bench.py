@@ -596,7 +596,7 @@ def main():
              "head_algorithmic_GBps": round(head_b / (head_us * 1e-6) / 1e9, 1),
              "note": "trunk entry (expand), unweighted exit (mean) and gated-head exit at "
                      "T=4096 S=4 H=4096; HIP events per call; bytes count each operand once "
-                     "(the head's split path reads x twice)"}
+                     "(from 256 tokens the head runs on the fused token tiles and reads x once)"}
     del emb, xs, hg
 
     # ---- decode-exact batching: a 64-token verify batch and the prefill chunk

@@ -515,9 +515,19 @@ int mhc_head(const float* x, const float* fn_w, const float* scale, const float*
   int rc = mhc_head_check(x, fn_w, scale, base, T, streams, hidden, eps, gates, y);
   if (rc || T == 0) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // The site's solo K-split over the same slab, S rows, in passes of at most
-  // kExactChunk tokens so that the partials stay bounded.
   const int S = streams, H = hidden, n = S * H;
+  if (T >= kFusedMinTokens && mhc::fused_supported(S, H)) {
+    // Large batches with a slab that fits on chip: the site's token tiles with the
+    // head's S rows, x read once.
+    Scratch sc;
+    if ((rc = get_scratch(mhc::fused_head_pack_bytes(S, H), &sc))) return rc;
+    return mhc::launch_fused_head(x, fn_w, scale, base, T, S, H, eps, gates, y, sc.general,
+                                  st) == hipSuccess
+               ? MHC_OK
+               : MHC_EHIP;
+  }
+  // Otherwise the site's solo K-split over the same slab, S rows, in passes of at
+  // most kExactChunk tokens so that the partials stay bounded.
   const PrePlan p1 = plan_pre(1, S, H);
   const int chunk = T < kExactChunk ? T : kExactChunk;
   Scratch sc;

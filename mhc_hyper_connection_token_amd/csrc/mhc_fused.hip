@@ -37,10 +37,9 @@ namespace mhc {
 // fn_w[4rg + j][c*H + 64*(w*CPW + u) + 4b .. +3] with c = ci / CPW, u = ci % CPW
 // (zero past the last row or column), so that every weight fetch of the fused
 // kernel is one contiguous kilobyte per wavefront.
-template <int S, int CPW>
+template <int S, int R, int CPW>
 __global__ __launch_bounds__(256) void pack_weight_kernel(const float* __restrict__ fn_w, int H,
                                                           float4* __restrict__ packed) {
-  constexpr int R = (2 + S) * S;
   constexpr int RG = (R + 3) / 4;
   constexpr int NCH = S * CPW;
   constexpr int TOTAL = 8 * NCH * RG * 64;
@@ -59,13 +58,14 @@ __global__ __launch_bounds__(256) void pack_weight_kernel(const float* __restric
                   : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-template <int S, int CPW, int WD, bool ZQ, bool POST>
+template <int S, int CPW, int WD, bool ZQ, bool POST, bool HEAD = false>
 __global__ __launch_bounds__(512) void fused_pre_kernel(
     const float* __restrict__ x, const float4* __restrict__ wpack,
     const float* __restrict__ scale, const float* __restrict__ base, int T, int H, int iters,
     float eps, float* __restrict__ pre, float* __restrict__ post, float* __restrict__ comb,
     float* __restrict__ y, Zq8Out zq, PostIn pin) {
-  constexpr int R = (2 + S) * S;
+  static_assert(!HEAD || (!ZQ && !POST), "the head has no epilogue and no post half");
+  constexpr int R = HEAD ? S : (2 + S) * S;
   constexpr int RG = (R + 3) / 4;  // weight-row groups of 4
   constexpr int NW = 8;
   constexpr int NOUT = 4 * (R + 1);
@@ -77,7 +77,15 @@ __global__ __launch_bounds__(512) void fused_pre_kernel(
   __shared__ float zred[ZQ ? NW : 1][4];
   __shared__ float gpc[POST ? 4 : 1][POST ? S * (S + 1) : 1];  // post gates, then comb [j][k]
 
-  stage_site_params(scale, base, R, params);
+  if constexpr (HEAD) {
+    // the head's single scale at 0 and its S biases from 3 on (pre_gate's layout)
+    if (threadIdx.x == 0)
+      params[0] = scale[0];
+    else if (threadIdx.x >= 3 && threadIdx.x < 3 + S)
+      params[threadIdx.x] = base[threadIdx.x - 3];
+  } else {
+    stage_site_params(scale, base, R, params);
+  }
   if constexpr (POST) {
     // the previous site's gates of the tile's tokens (a barrier follows below)
     constexpr int G1 = S * (S + 1);
@@ -232,8 +240,18 @@ __global__ __launch_bounds__(512) void fused_pre_kernel(
   }
   __syncthreads();
 
-  // ---- gates + Sinkhorn of the four tokens in wave 0
-  if (wave == 0) {
+  // ---- gates + Sinkhorn of the four tokens in wave 0 (the head: its sigmoid
+  // gates alone, lane 4u + c for token u, stream c)
+  if (HEAD) {
+    if (wave == 0 && lane < 16) {
+      const int u = lane >> 2, c = lane & 3;
+      if (c < S && t0 + u < T) {
+        const float g = pre_gate(&mr[u][0], c, R, n, eps, params);
+        pre[(size_t)(t0 + u) * S + c] = g;
+        pre_lds[u * 8 + c] = g;
+      }
+    }
+  } else if (wave == 0) {
     const int ntok = min(4, T - t0);
     gates_wave<4>(&mr[0][0], R + 1, ntok, S, n, params, iters, eps, true,
                   pre + (size_t)t0 * S, post + (size_t)t0 * S, comb + (size_t)t0 * S * S,
@@ -319,10 +337,13 @@ bool fused_supported(int S, int H) {
   return cpw <= 16 && S * cpw <= 32;
 }
 
-size_t fused_pack_bytes(int S, int H) {
-  const int R = (2 + S) * S, RG = (R + 3) / 4;
-  return (size_t)8 * S * fused_cpw(H) * RG * 64 * sizeof(float4);
+static size_t pack_bytes_rows(int S, int R, int H) {
+  return (size_t)8 * S * fused_cpw(H) * ((R + 3) / 4) * 64 * sizeof(float4);
 }
+
+size_t fused_pack_bytes(int S, int H) { return pack_bytes_rows(S, (2 + S) * S, H); }
+
+size_t fused_head_pack_bytes(int S, int H) { return pack_bytes_rows(S, S, H); }
 
 hipError_t launch_fused_pre(const float* x, const float* fn_w, const float* scale,
                             const float* base, int T, int S, int H, int iters, float eps,
@@ -340,8 +361,8 @@ hipError_t launch_fused_pre(const float* x, const float* fn_w, const float* scal
                      base, T, H, iters, eps, pre, post, comb, y, zv, pv)
 #define MHC_FU(SS, CC)                                                                        \
   if (S == SS && cpw == CC) {                                                                 \
-    hipLaunchKernelGGL((pack_weight_kernel<SS, CC>), dim3((total + 255) / 256), dim3(256), 0, \
-                       st, fn_w, H, pk);                                                      \
+    hipLaunchKernelGGL((pack_weight_kernel<SS, (2 + SS) * SS, CC>), dim3((total + 255) / 256), \
+                       dim3(256), 0, st, fn_w, H, pk);                                        \
     if (pin) {                                                                                \
       if (zq)                                                                                 \
         MHC_FK(SS, CC, true, true);                                                           \
@@ -361,6 +382,33 @@ hipError_t launch_fused_pre(const float* x, const float* fn_w, const float* scal
   MHC_FU(4, 1) MHC_FU(4, 2) MHC_FU(4, 4) MHC_FU(4, 8)
 #undef MHC_FU
 #undef MHC_FK
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fused_head(const float* x, const float* fn_h, const float* scale_h,
+                             const float* base_h, int T, int S, int H, float eps, float* gates,
+                             float* y, float* wpack, hipStream_t st) {
+  if (!fused_supported(S, H)) return hipErrorInvalidValue;
+  const int cpw = fused_cpw(H);
+  const int total = (int)(fused_head_pack_bytes(S, H) / sizeof(float4));
+  float4* pk = reinterpret_cast<float4*>(wpack);
+  const Zq8Out zv{nullptr, 0.f, nullptr, nullptr, nullptr};
+  const PostIn pv{nullptr, nullptr, nullptr, nullptr};
+  dim3 grid((T + 3) / 4);
+#define MHC_FH(SS, CC)                                                                        \
+  if (S == SS && cpw == CC) {                                                                 \
+    hipLaunchKernelGGL((pack_weight_kernel<SS, SS, CC>), dim3((total + 255) / 256), dim3(256), \
+                       0, st, fn_h, H, pk);                                                   \
+    hipLaunchKernelGGL((fused_pre_kernel<SS, CC, 1, false, false, true>), grid, dim3(512), 0,  \
+                       st, x, pk, scale_h, base_h, T, H, 1, eps, gates, nullptr, nullptr, y,  \
+                       zv, pv);                                                               \
+    return hipGetLastError();                                                                 \
+  }
+  MHC_FH(1, 1) MHC_FH(1, 2) MHC_FH(1, 4) MHC_FH(1, 8) MHC_FH(1, 16)
+  MHC_FH(2, 1) MHC_FH(2, 2) MHC_FH(2, 4) MHC_FH(2, 8) MHC_FH(2, 16)
+  MHC_FH(3, 1) MHC_FH(3, 2) MHC_FH(3, 4) MHC_FH(3, 8)
+  MHC_FH(4, 1) MHC_FH(4, 2) MHC_FH(4, 4) MHC_FH(4, 8)
+#undef MHC_FH
   return hipErrorInvalidValue;
 }
 

@@ -55,6 +55,14 @@ hipError_t launch_fused_pre(const float* x, const float* fn_w, const float* scal
                             float* pre, float* post, float* comb, float* y, float* wpack,
                             const Zq8Out* zq, const PostIn* pin, hipStream_t st);
 
+// The gated head (R = S rows, one scale, S biases, sigmoid gates, collapse) on
+// the same token tiles, for the shapes fused_supported() accepts; wpack holds
+// fused_head_pack_bytes(S, H) bytes.
+size_t fused_head_pack_bytes(int S, int H);
+hipError_t launch_fused_head(const float* x, const float* fn_h, const float* scale_h,
+                             const float* base_h, int T, int S, int H, float eps, float* gates,
+                             float* y, float* wpack, hipStream_t st);
+
 // Single-launch pre chain and branch-input epilogue of one token (S <= 4,
 // H % 32 == 0; decode_zq8_supported): split-K partials into `part` (same G /
 // chunks_per_range as the two-kernel path), the last block (ticket on
