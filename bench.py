@@ -407,9 +407,9 @@ def load_traffic(kernel):
 
 # prefill kernels whose counters make up each measured unit
 TRAFFIC_UNITS = {
-    "pre_call": ["pack_weight_kernel<4, 8>", "fused_pre_kernel<4, 8, 1, false, false>"],
+    "pre_call": ["pack_weight_kernel<4, 24, 8>", "fused_pre_kernel<4, 8, 1, false, false, false>"],
     "post_kernel": ["post_kernel<4>"],
-    "walk_call": ["pack_weight_kernel<4, 8>", "fused_pre_kernel<4, 8, 1, false, true>"],
+    "walk_call": ["pack_weight_kernel<4, 24, 8>", "fused_pre_kernel<4, 8, 1, false, true, false>"],
 }
 
 
