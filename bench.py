@@ -5,8 +5,8 @@ A step is one whole site over one batch of synthetic input already resident in
 HBM: mhc_site_pre (mixes, RMS rescale, gates, Sinkhorn, collapse) followed by
 mhc_site_post (post mix).  The timed workload is the prefill chunk (T=4096
 tokens, 4 streams, hidden 4096, 20 Sinkhorn iterations, eps 1e-6): `value` is
-its token throughput, timed as back-to-back replays of the site captured once
-in a HIP graph (the eager per-call figures ride along).  The same JSON line carries the decode site (T=1) in
+its token throughput, timed as one replay of the K sites captured in a HIP
+graph (the eager per-call figures ride along).  The same JSON line carries the decode site (T=1) in
 microseconds per site, the HBM roofline of the dominant kernel, and the CPU
 oracle's throughput on the host as a baseline.
 
@@ -115,25 +115,25 @@ def time_site(mhc, torch, t, c, out_pre, out_x, steps, warmup):
     pre_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
     post_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
 
-    # The timed steps: one site (pre + post) captured in a HIP graph and replayed
-    # `steps` times back to back, so that only device time and the gaps between
-    # kernels count (the scratch was sized by the eager calls above).
+    # The timed steps: the `steps` sites (pre + post each) captured in one HIP
+    # graph, as a trunk captures its sites, and replayed once, so that only
+    # device time and the gaps between kernels count.  One untimed replay first
+    # (the scratch was sized by the eager calls above).
     side = torch.cuda.Stream()
     side.wait_stream(stream)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side):
-        mhc.site_pre(t["x"], t["fn_w"], t["scale"], t["base"], c.iters, c.eps, out=out_pre)
-        mhc.site_post(t["x"], t["f"], out_pre[1], out_pre[2], out=out_x)
+        for _ in range(steps):
+            mhc.site_pre(t["x"], t["fn_w"], t["scale"], t["base"], c.iters, c.eps, out=out_pre)
+            mhc.site_post(t["x"], t["f"], out_pre[1], out_pre[2], out=out_x)
     torch.cuda.synchronize()
     with torch.cuda.stream(side):
-        for _ in range(warmup):
-            g.replay()
+        g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     with torch.cuda.stream(side):
         start.record(side)
-        for _ in range(steps):
-            g.replay()
+        g.replay()
         end.record(side)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -318,7 +318,9 @@ def time_walk(mhc, torch, c, x0, L, steps, warmup):
         mhc.site_post(x, sites[-1]["f"], o[1], o[2], out=xs[1 + L % 2])
 
     return (time_calls(torch, separate, steps, warmup) / L,
-            time_calls(torch, fused, steps, warmup) / L)
+            time_calls(torch, fused, steps, warmup) / L,
+            time_graph(torch, separate, calls=4, reps=3) / L,
+            time_graph(torch, fused, calls=4, reps=3) / L)
 
 
 def time_decode_walk(mhc, torch, c, x0, L=50, zq8=False):
@@ -581,20 +583,24 @@ def main():
     epi_us = zq_pre_us - pre_ms * 1e3
 
     # ---- a walk over 8 sites: separate calls against the fused post-then-pre schedule
-    walk_sep_us, walk_fused_us = time_walk(mhc, torch, c, t["x"], 8, max(3, args.steps // 5),
-                                           2)
+    walk_sep_us, walk_fused_us, walk_sep_g_us, walk_fused_g_us = time_walk(
+        mhc, torch, c, t["x"], 8, max(3, args.steps // 5), 2)
     walk_traffic = load_traffic("walk_call")
     walk = {"sites": 8,
             "separate_us_per_site": round(walk_sep_us, 2),
             "fused_us_per_site": round(walk_fused_us, 2),
-            "fused_tokens_per_s": round(c.T / (walk_fused_us * 1e-6), 1),
-            "fused_equivalent_GBps": round((pre_b + post_b) / (walk_fused_us * 1e-6) / 1e9, 1),
+            "separate_graph_us_per_site": round(walk_sep_g_us, 2),
+            "fused_graph_us_per_site": round(walk_fused_g_us, 2),
+            "fused_tokens_per_s": round(c.T / (walk_fused_g_us * 1e-6), 1),
+            "fused_equivalent_GBps": round((pre_b + post_b) / (walk_fused_g_us * 1e-6) / 1e9, 1),
             "fused_call_traffic": walk_traffic,
-            "fused_traffic_GBps": (round(walk_traffic / (walk_fused_us * 1e-6) / 1e9, 1)
+            "fused_traffic_GBps": (round(walk_traffic / (walk_fused_g_us * 1e-6) / 1e9, 1)
                                    if walk_traffic else None),
             "note": "prefill chunk, 8 sites with their own weights; fused: each site's post "
                     "and the next site's pre in one kernel (mhc_site_post_pre), bit-identical "
-                    "to the separate calls.  equivalent_GBps counts one pre + post's "
+                    "to the separate calls.  *_us_per_site: eager walks with HIP events; "
+                    "*_graph_us_per_site: 4 walks captured in one HIP graph, replayed; the "
+                    "rates use the graph figure.  equivalent_GBps counts one pre + post's "
                     "algorithmic bytes (the fused call does not re-read the new state); "
                     "traffic_GBps is the measured HBM bytes of the fused call (pack + kernel) "
                     "per site time"}
@@ -660,11 +666,11 @@ def main():
                      "pre_us": round(pre_ms * 1e3, 2), "post_us": round(post_ms * 1e3, 2),
                      "eager_ms_per_step": round(eager_ms, 4),
                      "algorithmic_bytes_per_step": pre_b + post_b,
-                     "note": "ms_per_step: the site (pre + post) captured once in a HIP graph "
-                             "and replayed `steps` times back to back, HIP events around the "
-                             "replays; eager_ms_per_step: the same steps as plain calls with an "
-                             "event between the calls, whose per-call times give pre_us and "
-                             "post_us"},
+                     "note": "ms_per_step: the `steps` sites (pre + post each) captured in one "
+                             "HIP graph and replayed once after one untimed replay, HIP events "
+                             "around the replay; eager_ms_per_step: the same steps as plain "
+                             "calls with an event between the calls, whose per-call times give "
+                             "pre_us and post_us"},
         "decode_t1": {"us_per_site": round(d_graph_us, 3), "eager_us_per_site": round(d_eager_us, 3),
                       "workspace_graph_us_per_site": round(d_ws_us, 3),
                       "walk_graph_us_per_site": round(d_walk_us, 3),
