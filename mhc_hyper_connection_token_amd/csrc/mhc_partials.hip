@@ -25,8 +25,10 @@
 
 namespace mhc {
 
+// Two waves per SIMD at least: the register bound keeps the three operand sets
+// of the chunk loop from dropping the kernel to one wave per SIMD.
 template <int NRT, int NTT>
-__global__ __launch_bounds__(256) void partials_kernel(const float* __restrict__ x,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void partials_kernel(const float* __restrict__ x,
                                                        const float* __restrict__ fn_w, int T,
                                                        int n, int R, int chunks_per_range,
                                                        float* __restrict__ part) {

@@ -90,8 +90,9 @@ __device__ __forceinline__ void block_partials(const float* __restrict__ x,
     xrow[tt] = x + (size_t)(xvalid[tt] ? t : 0) * n;
   }
 
-  // Double-buffered chunk loop: the loads of chunk c + 4 are issued before the
-  // MFMAs of chunk c.  Loads are branch-free (clamped addresses) and the
+  // Chunk loop over three operand sets: the loads of chunk c + 8 are issued
+  // before the MFMAs of chunk c, so two chunks are in flight behind the one
+  // being consumed.  Loads are branch-free (clamped addresses) and the
   // out-of-range lanes are zeroed by a select when the chunk is consumed.
   auto load_chunk = [&](int c, float4* a, float4* b) {
     const int k = c * 16 + kq;
@@ -104,12 +105,9 @@ __device__ __forceinline__ void block_partials(const float* __restrict__ x,
   auto sel = [](bool ok, float4 v) {
     return make_float4(ok ? v.x : 0.f, ok ? v.y : 0.f, ok ? v.z : 0.f, ok ? v.w : 0.f);
   };
-  float4 a0[NRT], b0[NTT], a1[NRT], b1[NTT];
-  int c = c_beg + wave;
-  if (c < c_end) load_chunk(c, a0, b0);
-  while (c < c_end) {
-    const int cn = c + 4;
-    if (cn < c_end) load_chunk(cn, a1, b1);
+  // The MFMAs of one chunk, on operands a0 / b0 (zeroed outside the valid
+  // rows, tokens and K).
+  auto consume = [&](int c, const float4* a0, const float4* b0) {
     const bool kin = c * 16 + kq < n;  // n % 4 == 0: a float4 is fully in or fully out
     float4 a[NRT], b[NTT];
 #pragma unroll
@@ -123,9 +121,6 @@ __device__ __forceinline__ void block_partials(const float* __restrict__ x,
       ss[tt] = fmaf(b[tt].z, b[tt].z, ss[tt]);
       ss[tt] = fmaf(b[tt].w, b[tt].w, ss[tt]);
     }
-    // Component-major issue: consecutive MFMAs go to different accumulators, so
-    // none waits for the previous one (each accumulator still adds x, y, z, w
-    // in that order).
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
@@ -146,11 +141,25 @@ __device__ __forceinline__ void block_partials(const float* __restrict__ x,
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt)
         acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rt].w, b[tt].w, acc[rt][tt], 0, 0, 0);
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) a0[rt] = a1[rt];
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) b0[tt] = b1[tt];
-    c = cn;
+  };
+  // three operand sets in a ring: chunk c + 8 is requested while chunk c is
+  // consumed (the ring is unrolled so every set stays in named registers)
+  float4 a0[NRT], b0[NTT], a1[NRT], b1[NTT], a2[NRT], b2[NTT];
+  int c = c_beg + wave;
+  if (c < c_end) load_chunk(c, a0, b0);
+  if (c + 4 < c_end) load_chunk(c + 4, a1, b1);
+  while (c < c_end) {
+    if (c + 8 < c_end) load_chunk(c + 8, a2, b2);
+    consume(c, a0, b0);
+    c += 4;
+    if (c >= c_end) break;
+    if (c + 8 < c_end) load_chunk(c + 8, a0, b0);
+    consume(c, a1, b1);
+    c += 4;
+    if (c >= c_end) break;
+    if (c + 8 < c_end) load_chunk(c + 8, a1, b1);
+    consume(c, a2, b2);
+    c += 4;
   }
 
   // Sum of squares: lanes l, l^16, l^32, l^48 hold the same token's partials.
