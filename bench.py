@@ -568,6 +568,26 @@ def main():
     d_walk_zq_us = time_decode_walk(mhc, torch, cd, td["x"], zq8=True)
     pre1, post1 = algorithmic_bytes(cd.T, cd.S, cd.H)
 
+    # ---- verify-batch sites (T = 4 and 8): pre, post and the whole site, each
+    # from a HIP graph of 50 calls (device time plus the gaps between kernels)
+    verify = {}
+    for vname in ("verify4", "verify8"):
+        cv = CONFIGS[vname]
+        tv = to_dev(make_site(cv), torch)
+        vpre, vx = alloc_out(cv.T, cv.S, cv.H, torch)
+        v_pre_us = time_graph(torch, lambda: mhc.site_pre(
+            tv["x"], tv["fn_w"], tv["scale"], tv["base"], cv.iters, cv.eps, out=vpre),
+            calls=50, reps=10)
+        v_post_us = time_graph(torch, lambda: mhc.site_post(
+            tv["x"], tv["f"], vpre[1], vpre[2], out=vx), calls=50, reps=10)
+        _, v_site_us = time_decode(mhc, torch, tv, cv, vpre, vx, 500)
+        verify[f"T{cv.T}"] = {"pre_us": round(v_pre_us, 3), "post_us": round(v_post_us, 3),
+                              "site_us": round(v_site_us, 3),
+                              "tokens_per_s": round(cv.T / (v_site_us * 1e-6), 1)}
+    verify["note"] = ("verify batches (S=4, H=4096, 20 iterations): pre alone, post alone and "
+                      "the whole site, each as 50 calls in a HIP graph replayed, HIP-event time "
+                      "per call")
+
     # ---- branch-input epilogue (RMS norm of y with a weight, q8 codes): the pre
     # call with it, against the same call without it
     from mhc_inputs import make_norm_weight
@@ -671,6 +691,7 @@ def main():
                              "around the replay; eager_ms_per_step: the same steps as plain "
                              "calls with an event between the calls, whose per-call times give "
                              "pre_us and post_us"},
+        "verify_sites": verify,
         "decode_t1": {"us_per_site": round(d_graph_us, 3), "eager_us_per_site": round(d_eager_us, 3),
                       "workspace_graph_us_per_site": round(d_ws_us, 3),
                       "walk_graph_us_per_site": round(d_walk_us, 3),
