@@ -584,6 +584,35 @@ def main():
         verify[f"T{cv.T}"] = {"pre_us": round(v_pre_us, 3), "post_us": round(v_post_us, 3),
                               "site_us": round(v_site_us, 3),
                               "tokens_per_s": round(cv.T / (v_site_us * 1e-6), 1)}
+    # ---- wide site (T = 1024, S = 8, H = 7168): the split path, bound by the
+    # fp32 MFMA rate of its partials (33 flop per byte)
+    cw = CONFIGS["wide"]
+    tw = to_dev(make_site(cw), torch)
+    wpre, wx = alloc_out(cw.T, cw.S, cw.H, torch)
+    w_pre_us = time_graph(torch, lambda: mhc.site_pre(
+        tw["x"], tw["fn_w"], tw["scale"], tw["base"], cw.iters, cw.eps, out=wpre), calls=10, reps=5)
+    w_post_us = time_graph(torch, lambda: mhc.site_post(
+        tw["x"], tw["f"], wpre[1], wpre[2], out=wx), calls=10, reps=5)
+
+    def wide_site():
+        mhc.site_pre(tw["x"], tw["fn_w"], tw["scale"], tw["base"], cw.iters, cw.eps, out=wpre)
+        mhc.site_post(tw["x"], tw["f"], wpre[1], wpre[2], out=wx)
+    w_site_us = time_graph(torch, wide_site, calls=10, reps=5)
+    wpre_b, wpost_b = algorithmic_bytes(cw.T, cw.S, cw.H)
+    w_rows = (2 + cw.S) * cw.S
+    w_flop = 2.0 * cw.T * w_rows * cw.S * cw.H  # the mixes contraction
+    wide = {"T": cw.T, "streams": cw.S, "hidden": cw.H,
+            "pre_us": round(w_pre_us, 2), "post_us": round(w_post_us, 2),
+            "site_us": round(w_site_us, 2),
+            "tokens_per_s": round(cw.T / (w_site_us * 1e-6), 1),
+            "algorithmic_GBps": round((wpre_b + wpost_b) / (w_site_us * 1e-6) / 1e9, 1),
+            "pre_mixes_TFLOPs": round(w_flop / (w_pre_us * 1e-6) / 1e12, 2),
+            "note": "generalised width; pre, post and site each as 10 calls in a HIP graph "
+                    "replayed; pre_mixes_TFLOPs is the fp32 mixes contraction (2*T*R*S*H flop) "
+                    "over the whole pre call (partials + finish), against 157.3 TFLOP/s"}
+    del tw, wpre, wx
+    torch.cuda.empty_cache()
+
     verify["note"] = ("verify batches (S=4, H=4096, 20 iterations): pre alone, post alone and "
                       "the whole site, each as 50 calls in a HIP graph replayed, HIP-event time "
                       "per call")
@@ -692,6 +721,7 @@ def main():
                              "calls with an event between the calls, whose per-call times give "
                              "pre_us and post_us"},
         "verify_sites": verify,
+        "wide_site": wide,
         "decode_t1": {"us_per_site": round(d_graph_us, 3), "eager_us_per_site": round(d_eager_us, 3),
                       "workspace_graph_us_per_site": round(d_ws_us, 3),
                       "walk_graph_us_per_site": round(d_walk_us, 3),
