@@ -68,7 +68,11 @@ def test_mean_inverts_expand(mhc, S):
 
 
 @pytest.mark.parametrize("T,S,H", [(1, 4, 4096), (2, 1, 64), (5, 2, 1024), (17, 3, 132),
-                                   (64, 8, 512), (300, 4, 1056), (3, 4, 16384), (9000, 1, 32)])
+                                   (64, 8, 512), (300, 4, 1056), (3, 4, 16384), (9000, 1, 32),
+                                   # the fused token tiles (from 256 tokens, S <= 4): ragged
+                                   # last tiles, a slab width past the last full column block
+                                   (255, 4, 4096), (256, 2, 2052), (259, 3, 1028),
+                                   (1001, 4, 4096), (300, 8, 256)])
 def test_head_matches_oracle(mhc, T, S, H):
     print(f"[case] head T{T} S{S} H{H}", flush=True)
     x = make_random_shape(T, S, H, seed=T + 11 * S)["x"]
@@ -108,6 +112,38 @@ def test_head_with_site_pre_rows_matches_the_site(mhc):
     torch.cuda.synchronize()
     assert_gates_close(g.cpu().numpy(), pre.cpu().numpy().astype(np.float64), "head vs site")
     assert_streams_close(y.cpu().numpy(), ys.cpu().numpy().astype(np.float64), "head y vs site")
+
+
+def test_head_graph_replays_match_eager(mhc):
+    # the fused head packs its weight into the library scratch on every call
+    T, S, H = 260, 4, 2048
+    print(f"[case] head graph T{T} S{S} H{H}", flush=True)
+    x = _dev(make_random_shape(T, S, H, seed=41)["x"])
+    x2 = _dev(make_random_shape(T, S, H, seed=42)["x"])
+    w, scale, base = (_dev(a) for a in _head_weights(S, H, seed=43))
+    w2, scale2, base2 = (_dev(a) for a in _head_weights(S, H, seed=44))
+    out = (torch.empty((T, S), device="cuda"), torch.empty((T, H), device="cuda"))
+    oth = (torch.empty((T, S), device="cuda"), torch.empty((T, H), device="cuda"))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        mhc.head(x, w, scale, base, 1e-6, out=out)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in out]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        mhc.head(x, w, scale, base, 1e-6, out=out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in out:
+            t.fill_(float("nan"))
+        with torch.cuda.stream(s):
+            mhc.head(x2, w2, scale2, base2, 1e-6, out=oth)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("gates", "y"), out, ref):
+            assert torch.equal(a, b), f"replay {rep}: head {name} differs from the eager result"
 
 
 def test_trunk_zero_tokens(mhc):
