@@ -17,6 +17,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -187,6 +188,69 @@ def time_decode(mhc, torch, t, c, out_pre, out_x, sites, graph_sites=50, zq8=Non
     torch.cuda.synchronize()
     graph_us = a.elapsed_time(b) * 1e3 / (reps * graph_sites)
     return eager_us, graph_us
+
+
+def time_cold_decode(mhc, torch, c, sets=200, reps=5):
+    """Decode sites (T=1) rotating through `sets` distinct weight / state / branch
+    sets (1.5 MiB of weight each at 4 x 4096, so 200 sets exceed the 256 MB
+    memory-side cache), one HIP graph of `sets` sites, replayed; against the
+    same graph over one set.  Returns µs per site for both."""
+    from mhc_inputs import make_random_shape
+    base_set = make_random_shape(c.T, c.S, c.H, seed=1)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    R = (2 + c.S) * c.S
+    pool = []
+    for _ in range(sets):
+        pool.append({
+            "x": torch.rand((c.T, c.S, c.H), device="cuda", generator=g) * 2 - 1,
+            "fn_w": torch.randn((R, c.S * c.H), device="cuda", generator=g) / (c.S * c.H) ** 0.5,
+            "scale": torch.rand(3, device="cuda", generator=g) + 0.5,
+            "base": torch.randn(R, device="cuda", generator=g) * 0.1 ** 0.5,
+            "f": torch.rand((c.T, c.H), device="cuda", generator=g) * 2 - 1})
+    warm = to_dev(base_set, torch)
+    (o_pre, o_x) = alloc_out(c.T, c.S, c.H, torch)
+
+    def graph_us(seq):
+        def run():
+            for st in seq:
+                mhc.site_pre(st["x"], st["fn_w"], st["scale"], st["base"], c.iters, c.eps,
+                             out=o_pre)
+                mhc.site_post(st["x"], st["f"], o_pre[1], o_pre[2], out=o_x)
+        return time_graph(torch, run, calls=1, reps=reps) / len(seq)
+    cold_us = graph_us(pool)
+    warm_us = graph_us([warm] * sets)
+    del pool
+    torch.cuda.empty_cache()
+    return {"sets": sets, "cold_us_per_site": round(cold_us, 3),
+            "warm_us_per_site": round(warm_us, 3),
+            "note": "decode sites (T=1, S=4, H=4096) in one HIP graph: cold rotates through "
+                    "distinct weight/state/branch sets (about 1.6 MB each, more than the "
+                    "memory-side cache in total); warm repeats one set"}
+
+
+def run_bandwidth_probe(mhc, torch, gib=1, reps=20):
+    """HBM rate of a plain stream on this part: mhc_bandwidth_probe copying and
+    reading `gib` GiB (streaming 16-byte loads and stores), HIP events around
+    `reps` calls."""
+    n = (gib << 30) // 4
+    src = torch.empty(n, device="cuda", dtype=torch.float32).uniform_(-1, 1)
+    dst = torch.empty_like(src)
+    sink = torch.empty(int(mhc.load_library().mhc_probe_sink_floats(n * 4)), device="cuda",
+                       dtype=torch.float32)
+    copy_us = time_calls(torch, lambda: mhc.bandwidth_probe(src, dst, True), reps, 3)
+    read_us = time_calls(torch, lambda: mhc.bandwidth_probe(src, sink, False), reps, 3)
+    nbytes = n * 4
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    copy_gbps = 2 * nbytes / (copy_us * 1e-6) / 1e9
+    read_gbps = nbytes / (read_us * 1e-6) / 1e9
+    return {"bytes": nbytes, "copy_us": round(copy_us, 2), "read_us": round(read_us, 2),
+            "copy_GBps": round(copy_gbps, 1), "read_GBps": round(read_gbps, 1),
+            "copy_frac_of_peak": round(copy_gbps / PEAK_HBM_GBPS, 4),
+            "read_frac_of_peak": round(read_gbps / PEAK_HBM_GBPS, 4),
+            "note": "mhc_bandwidth_probe: a plain copy (read + write counted) and a plain "
+                    "read of 1 GiB, the rate a pure stream reaches on this part against the "
+                    "published 8 TB/s"}
 
 
 def time_pre_zq8(mhc, torch, t, c, nw, norm_eps, out7, steps, warmup):
@@ -568,6 +632,29 @@ def main():
     d_walk_zq_us = time_decode_walk(mhc, torch, cd, td["x"], zq8=True)
     pre1, post1 = algorithmic_bytes(cd.T, cd.S, cd.H)
 
+    # ---- decode: the Sinkhorn's share (iters sweep, least-squares line over
+    # µs per site) and a cold variant (weights rotating through more than the
+    # 256 MB memory-side cache)
+    sweep_iters = (1, 5, 10, 20, 40)
+    it_us = []
+    for it in sweep_iters:
+        cit = dataclasses.replace(cd, iters=it)
+        it_us.append(time_decode(mhc, torch, td, cit, dpre, dx, 500)[1])
+    mx = sum(sweep_iters) / len(sweep_iters)
+    my = sum(it_us) / len(it_us)
+    slope = (sum((a - mx) * (b - my) for a, b in zip(sweep_iters, it_us))
+             / sum((a - mx) ** 2 for a in sweep_iters))
+    iters_sweep = {"iters": list(sweep_iters), "us_per_site": [round(v, 3) for v in it_us],
+                   "slope_us_per_iter": round(slope, 4),
+                   "intercept_us": round(my - slope * mx, 3),
+                   "note": "decode site (T=1) from a HIP graph of 50 sites at each Sinkhorn "
+                           "iteration count; slope = the Sinkhorn's cost per iteration, "
+                           "intercept = everything else"}
+    cold = time_cold_decode(mhc, torch, cd, sets=200)
+
+    # ---- pure-stream bandwidth of this part (mhc_bandwidth_probe over 1 GiB)
+    probe = run_bandwidth_probe(mhc, torch)
+
     # ---- verify-batch sites (T = 4 and 8): pre, post and the whole site, each
     # from a HIP graph of 50 calls (device time plus the gaps between kernels)
     verify = {}
@@ -721,6 +808,9 @@ def main():
                              "calls with an event between the calls, whose per-call times give "
                              "pre_us and post_us"},
         "verify_sites": verify,
+        "decode_iters_sweep": iters_sweep,
+        "decode_cold": cold,
+        "bandwidth_probe": probe,
         "wide_site": wide,
         "decode_t1": {"us_per_site": round(d_graph_us, 3), "eager_us_per_site": round(d_eager_us, 3),
                       "workspace_graph_us_per_site": round(d_ws_us, 3),

@@ -286,6 +286,24 @@ int mhc_site_pre_zq8_check(const float* x, const float* fn_w, const float* scale
 /* Static text for a return code (never NULL). */
 const char* mhc_status_string(int status);
 
+/*
+ * Bandwidth probe (a measurement aid, not part of the site program).  The
+ * hc_fused_gate.rs page's gate carries a bandwidth probe of its own, a pure
+ * streamer reporting read and read + write GB/s; this one gives the same two
+ * rates on this part, and the site kernels' rates are read against them.
+ *
+ * mhc_bandwidth_probe: with copy != 0, copies `bytes` from src to dst (both
+ *   `bytes` long, not overlapping); with copy == 0, reads `bytes` from src and
+ *   writes mhc_probe_sink_floats(bytes) block sums (one per 4 KiB of src) to
+ *   dst.  Streaming 16-byte loads (and stores), one quad per thread.
+ *   bytes % 16 == 0 and 16-byte aligned pointers (MHC_EALIGN otherwise); NULL
+ *   pointers are MHC_EINVAL; overlapping buffers MHC_EOVERLAP; more than 2^43
+ *   bytes MHC_EUNSUPPORTED; bytes == 0 does nothing.  Asynchronous on
+ *   `stream` like the site calls.
+ */
+size_t mhc_probe_sink_floats(size_t bytes);
+int mhc_bandwidth_probe(const float* src, float* dst, size_t bytes, int copy, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

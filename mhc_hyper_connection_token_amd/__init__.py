@@ -19,7 +19,7 @@ import os
 
 __all__ = ["site_pre", "site_post", "site_pre_zq8", "site_pre_check", "site_post_check",
            "site_pre_zq8_check", "site_post_pre", "site_post_pre_check", "expand", "mean",
-           "head", "head_check", "Workspace",
+           "head", "head_check", "bandwidth_probe", "Workspace",
            "workspace_bytes", "load_library", "MhcError", "LIB_PATH", "EXPORTED_SYMBOLS",
            "STATUS"]
 
@@ -32,7 +32,7 @@ EXPORTED_SYMBOLS = ("mhc_site_pre", "mhc_site_post", "mhc_site_pre_exact", "mhc_
                     "mhc_ws_site_pre", "mhc_ws_site_pre_zq8", "mhc_ws_site_post",
                     "mhc_expand", "mhc_mean", "mhc_head", "mhc_head_check",
                     "mhc_site_post_pre", "mhc_site_post_pre_zq8", "mhc_site_post_pre_check",
-                    "mhc_status_string")
+                    "mhc_status_string", "mhc_probe_sink_floats", "mhc_bandwidth_probe")
 
 STATUS = {0: "MHC_OK", 1: "MHC_EINVAL", 2: "MHC_EALIGN", 3: "MHC_EUNSUPPORTED",
           4: "MHC_EHIP", 5: "MHC_EOVERLAP"}
@@ -104,6 +104,10 @@ def load_library() -> ctypes.CDLL:
     lib.mhc_head.restype = i
     lib.mhc_head_check.argtypes = [vp, vp, vp, vp, i, i, i, fl, vp, vp]
     lib.mhc_head_check.restype = i
+    lib.mhc_probe_sink_floats.argtypes = [sz]
+    lib.mhc_probe_sink_floats.restype = sz
+    lib.mhc_bandwidth_probe.argtypes = [vp, vp, sz, i, vp]
+    lib.mhc_bandwidth_probe.restype = i
     if lib.mhc_workspace_struct_bytes() != ctypes.sizeof(_WsStruct):
         raise RuntimeError("mhc_workspace layout of the library and the binding differ")
     _lib = lib
@@ -356,6 +360,21 @@ def head(x, fn_w, scale, base, eps: float, *, out=None, stream=None):
     if rc != 0:
         raise MhcError("mhc_head", rc, _status_text(lib, rc))
     return out
+
+
+def bandwidth_probe(src, dst, copy: bool, *, stream=None):
+    """Pure-stream probe (mhc_bandwidth_probe): copy src into dst (same size), or
+    read src and write block sums into dst (probe_sink_floats(src) floats)."""
+    lib = load_library()
+    ps = _dev(src, "src")
+    want = src.numel() if copy else int(lib.mhc_probe_sink_floats(src.numel() * 4))
+    if dst.numel() != want:
+        raise ValueError(f"dst must hold {want} floats")
+    pd = _dev(dst, "dst")
+    rc = lib.mhc_bandwidth_probe(ps, pd, src.numel() * 4, int(bool(copy)), _stream_handle(stream))
+    if rc != 0:
+        raise MhcError("mhc_bandwidth_probe", rc, _status_text(lib, rc))
+    return dst
 
 
 def head_check(x_ptr, fn_w_ptr, scale_ptr, base_ptr, T, S, H, eps, gates_ptr, y_ptr) -> int:

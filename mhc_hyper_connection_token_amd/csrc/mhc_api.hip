@@ -460,6 +460,29 @@ int mhc_site_post(const float* x, const float* f, const float* post, const float
 
 }  // extern "C"
 
+// ---------------------------------------------------------------- bandwidth probe
+extern "C" {
+
+size_t mhc_probe_sink_floats(size_t bytes) {
+  return (size_t)mhc::probe_blocks((long)(bytes / 16));
+}
+
+int mhc_bandwidth_probe(const float* src, float* dst, size_t bytes, int copy, void* stream) {
+  if (bytes == 0) return MHC_OK;
+  int rc;
+  if ((rc = check_ptr(src)) || (rc = check_ptr(dst))) return rc;
+  if (bytes % 16 != 0) return MHC_EALIGN;
+  if (bytes / 16 / 256 >= 0x7fffffffUL) return MHC_EUNSUPPORTED;
+  const size_t dst_bytes = copy ? bytes : mhc_probe_sink_floats(bytes) * sizeof(float);
+  if (overlaps(span(src, bytes), span(dst, dst_bytes))) return MHC_EOVERLAP;
+  return mhc::launch_probe(src, dst, (long)(bytes / 16), copy != 0,
+                           static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MHC_OK
+             : MHC_EHIP;
+}
+
+}  // extern "C"
+
 // ---------------------------------------------------------------- trunk ends
 extern "C" {
 

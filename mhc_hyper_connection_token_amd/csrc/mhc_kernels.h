@@ -89,6 +89,11 @@ hipError_t launch_head_finish(const float* x, const float* part, int G, int T, i
                               const float* scale_h, const float* base_h, float eps, float* gates,
                               float* y, hipStream_t st);
 
+// Bandwidth probes: copy nq 16-byte quads from src to dst, or (copy false)
+// read them and write probe_blocks(nq) block sums to dst.
+long probe_blocks(long nq);
+hipError_t launch_probe(const float* src, float* dst, long nq, bool copy, hipStream_t st);
+
 // Post mix.
 hipError_t launch_post(const float* x, const float* f, const float* post, const float* comb,
                        int T, int S, int H, float* x_out, hipStream_t st);

@@ -270,3 +270,16 @@ def test_post_pre_check(lib):
                                    y2) == EINVAL
     assert mhc.site_post_pre_check(x, f, po, co, w, sc, b, T, 9, H, 20, 1e-6, xo, pre2, po2, co2,
                                    y2) == EUNSUP
+
+
+def test_bandwidth_probe_refuses_before_any_gpu_work(lib):
+    a, b = 4096, 4096 + (1 << 20)  # 16-byte aligned fake addresses, never touched
+    vp = ctypes.c_void_p
+    assert lib.mhc_bandwidth_probe(vp(a), vp(b), 0, 1, None) == OK  # nothing to do
+    assert lib.mhc_bandwidth_probe(None, vp(b), 64, 1, None) == EINVAL
+    assert lib.mhc_bandwidth_probe(vp(a), None, 64, 0, None) == EINVAL
+    assert lib.mhc_bandwidth_probe(vp(a + 4), vp(b), 64, 1, None) == EALIGN
+    assert lib.mhc_bandwidth_probe(vp(a), vp(b), 60, 1, None) == EALIGN
+    assert lib.mhc_bandwidth_probe(vp(a), vp(a + 32), 64, 1, None) == EOVERLAP
+    assert lib.mhc_probe_sink_floats(1 << 20) == (1 << 20) // 4096
+    assert lib.mhc_probe_sink_floats(16) == 1
