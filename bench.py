@@ -655,10 +655,11 @@ def main():
     # ---- pure-stream bandwidth of this part (mhc_bandwidth_probe over 1 GiB)
     probe = run_bandwidth_probe(mhc, torch)
 
-    # ---- verify-batch sites (T = 4 and 8): pre, post and the whole site, each
-    # from a HIP graph of 50 calls (device time plus the gaps between kernels)
+    # ---- small sites (the tiny config, the decode site, the verify batches):
+    # pre, post and the whole site, each from a HIP graph of 50 calls (device
+    # time plus the gaps between kernels)
     verify = {}
-    for vname in ("verify4", "verify8"):
+    for vname in ("tiny", "decode", "verify4", "verify8"):
         cv = CONFIGS[vname]
         tv = to_dev(make_site(cv), torch)
         vpre, vx = alloc_out(cv.T, cv.S, cv.H, torch)
@@ -668,7 +669,8 @@ def main():
         v_post_us = time_graph(torch, lambda: mhc.site_post(
             tv["x"], tv["f"], vpre[1], vpre[2], out=vx), calls=50, reps=10)
         _, v_site_us = time_decode(mhc, torch, tv, cv, vpre, vx, 500)
-        verify[f"T{cv.T}"] = {"pre_us": round(v_pre_us, 3), "post_us": round(v_post_us, 3),
+        verify[f"{vname}_T{cv.T}_H{cv.H}"] = {"pre_us": round(v_pre_us, 3),
+                              "post_us": round(v_post_us, 3),
                               "site_us": round(v_site_us, 3),
                               "tokens_per_s": round(cv.T / (v_site_us * 1e-6), 1)}
     # ---- wide site (T = 1024, S = 8, H = 7168): the split path, bound by the
@@ -700,9 +702,8 @@ def main():
     del tw, wpre, wx
     torch.cuda.empty_cache()
 
-    verify["note"] = ("verify batches (S=4, H=4096, 20 iterations): pre alone, post alone and "
-                      "the whole site, each as 50 calls in a HIP graph replayed, HIP-event time "
-                      "per call")
+    verify["note"] = ("small sites (S=4, 20 iterations): pre alone, post alone and the whole "
+                      "site, each as 50 calls in a HIP graph replayed, HIP-event time per call")
 
     # ---- branch-input epilogue (RMS norm of y with a weight, q8 codes): the pre
     # call with it, against the same call without it
@@ -807,7 +808,7 @@ def main():
                              "around the replay; eager_ms_per_step: the same steps as plain "
                              "calls with an event between the calls, whose per-call times give "
                              "pre_us and post_us"},
-        "verify_sites": verify,
+        "small_sites": verify,
         "decode_iters_sweep": iters_sweep,
         "decode_cold": cold,
         "bandwidth_probe": probe,
