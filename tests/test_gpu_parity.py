@@ -102,6 +102,10 @@ def test_config_parity_full_size_sampled(mhc, name):
     # batches large enough for the token-tiled fused kernel (S <= 4, T >= 256)
     (256, 4, 4096, 20), (259, 3, 1028, 20), (300, 2, 4, 5), (261, 4, 2052, 1),
     (257, 4, 68, 20), (320, 1, 8192, 20),
+    # S > 4 from 512 tokens: 64-token MFMA blocks with a partly empty last block
+    (513, 8, 1024, 20), (700, 6, 516, 20), (1000, 5, 260, 3), (577, 7, 128, 20),
+    # the fused tiles at S = 4 with a ragged last tile
+    (1025, 4, 1024, 20), (2047, 4, 2048, 1),
 ])
 def test_ragged_shapes(mhc, T, S, H, iters):
     _say(f"ragged T={T} S={S} H={H} iters={iters}")
