@@ -387,8 +387,8 @@ def time_walk(mhc, torch, c, x0, L, steps, warmup):
             time_graph(torch, fused, calls=4, reps=3) / L)
 
 
-def time_decode_walk(mhc, torch, c, x0, L=50, zq8=False):
-    """Decode sites (T=1) chained as a trunk runs them, four distinct site weights
+def time_decode_walk(mhc, torch, c, x0, L=50, zq8=False, distinct=4):
+    """Decode sites (T=1) chained as a trunk runs them, `distinct` site weights
     in rotation, in one HIP graph: the first pre, then mhc_site_post_pre per
     site, then the last post; with zq8 every pre carries the branch-input
     epilogue.  Returns µs per site (graph replay)."""
@@ -398,7 +398,8 @@ def time_decode_walk(mhc, torch, c, x0, L=50, zq8=False):
     sites = [{"fn_w": torch.randn((R, S * H), device="cuda", generator=g) / (S * H) ** 0.5,
               "scale": torch.rand(3, device="cuda", generator=g) + 0.5,
               "base": torch.randn(R, device="cuda", generator=g) * 0.1 ** 0.5,
-              "f": torch.rand((T, H), device="cuda", generator=g) * 2 - 1} for _ in range(4)]
+              "f": torch.rand((T, H), device="cuda", generator=g) * 2 - 1}
+             for _ in range(distinct)]
     nw = torch.rand(H, device="cuda", generator=g) + 0.5
     e = lambda *s, dt=torch.float32: torch.empty(s, device="cuda", dtype=dt)  # noqa: E731
     xs = [x0.clone(), e(T, S, H), e(T, S, H)]
@@ -415,14 +416,14 @@ def time_decode_walk(mhc, torch, c, x0, L=50, zq8=False):
             mhc.site_pre(xs[0], st["fn_w"], st["scale"], st["base"], c.iters, c.eps, out=o[:4])
         x = xs[0]
         for k in range(1, L):
-            st, prev = sites[k % 4], sites[(k - 1) % 4]
+            st, prev = sites[k % distinct], sites[(k - 1) % distinct]
             on = outs[k % 2]
             xn = xs[1 + k % 2]
             mhc.site_post_pre(x, prev["f"], o[1], o[2], st["fn_w"], st["scale"], st["base"],
                               c.iters, c.eps, nw=nw if zq8 else None,
                               out=(xn,) + tuple(on if zq8 else on[:4]))
             x, o = xn, on
-        mhc.site_post(x, sites[(L - 1) % 4]["f"], o[1], o[2], out=xs[1 + L % 2])
+        mhc.site_post(x, sites[(L - 1) % distinct]["f"], o[1], o[2], out=xs[1 + L % 2])
     return time_graph(torch, walk, calls=1, reps=20) / L
 
 
@@ -651,6 +652,10 @@ def main():
                            "iteration count; slope = the Sinkhorn's cost per iteration, "
                            "intercept = everything else"}
     cold = time_cold_decode(mhc, torch, cd, sets=200)
+    cold["walk_cold_us_per_site"] = round(
+        time_decode_walk(mhc, torch, cd, td["x"], L=200, distinct=200), 3)
+    cold["note"] += ("; walk_cold: 200 sites chained with mhc_site_post_pre, each with its "
+                     "own weight, one graph")
 
     # ---- pure-stream bandwidth of this part (mhc_bandwidth_probe over 1 GiB)
     probe = run_bandwidth_probe(mhc, torch)
