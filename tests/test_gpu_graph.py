@@ -36,7 +36,10 @@ def _alloc(T, S, H):
 
 
 @pytest.mark.parametrize("T,S,H", [(1, 4, 4096), (2, 8, 512), (8, 4, 4096), (130, 4, 1024),
-                                   (258, 4, 1024)])
+                                   (258, 4, 1024),
+                                   # the prefill chunk and the wide site, as the benchmark
+                                   # replays them (their eager outputs are parity-tested)
+                                   (4096, 4, 4096), (1024, 8, 7168)])
 def test_graph_replays_match_eager(mhc, T, S, H):
     print(f"[case] graph T={T} S={S} H={H}", flush=True)
     iters, eps = 20, 1e-6
