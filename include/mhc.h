@@ -52,7 +52,7 @@ enum {
   MHC_OK = 0,
   MHC_EINVAL = 1,      /* bad size, count, eps, iteration count or NULL pointer */
   MHC_EALIGN = 2,      /* H % 4 != 0 or a pointer not 16-byte aligned            */
-  MHC_EUNSUPPORTED = 3,/* valid arguments the library does not handle (S > 8)  */
+  MHC_EUNSUPPORTED = 3,/* valid arguments the library does not handle (S > 8, sizes too large) */
   MHC_EHIP = 4,        /* the HIP runtime reported an error (launch, allocation) */
   MHC_EOVERLAP = 5     /* an output buffer overlaps an input buffer              */
 };

@@ -164,7 +164,9 @@ const char* mhc_status_string(int status) {
     case MHC_OK: return "ok";
     case MHC_EINVAL: return "invalid argument (size, count, eps, iterations or NULL pointer)";
     case MHC_EALIGN: return "misaligned: hidden must be a multiple of 4 and pointers 16-byte aligned";
-    case MHC_EUNSUPPORTED: return "unsupported shape (streams > 8 or T*streams*hidden >= 2^31)";
+    case MHC_EUNSUPPORTED:
+      return "unsupported size (streams > 8, T*streams*hidden >= 2^31, or a larger buffer than "
+             "the call handles)";
     case MHC_EHIP: return "HIP runtime error";
     case MHC_EOVERLAP: return "an output buffer overlaps an input or another output";
     default: return "unknown status";
