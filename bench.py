@@ -190,6 +190,19 @@ def time_decode(mhc, torch, t, c, out_pre, out_x, sites, graph_sites=50, zq8=Non
     return eager_us, graph_us
 
 
+def fit_line(xs, ys):
+    """Least-squares line through the points (xs, ys): (slope, intercept)."""
+    n = len(xs)
+    if n < 2 or len(ys) != n:
+        raise ValueError("need at least two (x, y) points")
+    mx, my = sum(xs) / n, sum(ys) / n
+    sxx = sum((a - mx) ** 2 for a in xs)
+    if sxx == 0:
+        raise ValueError("the x values are all equal")
+    slope = sum((a - mx) * (b - my) for a, b in zip(xs, ys)) / sxx
+    return slope, my - slope * mx
+
+
 def time_cold_decode(mhc, torch, c, sets=200, reps=5):
     """Decode sites (T=1) rotating through `sets` distinct weight / state / branch
     sets (1.5 MiB of weight each at 4 x 4096, so 200 sets exceed the 256 MB
@@ -641,13 +654,10 @@ def main():
     for it in sweep_iters:
         cit = dataclasses.replace(cd, iters=it)
         it_us.append(time_decode(mhc, torch, td, cit, dpre, dx, 500)[1])
-    mx = sum(sweep_iters) / len(sweep_iters)
-    my = sum(it_us) / len(it_us)
-    slope = (sum((a - mx) * (b - my) for a, b in zip(sweep_iters, it_us))
-             / sum((a - mx) ** 2 for a in sweep_iters))
+    slope, intercept = fit_line(sweep_iters, it_us)
     iters_sweep = {"iters": list(sweep_iters), "us_per_site": [round(v, 3) for v in it_us],
                    "slope_us_per_iter": round(slope, 4),
-                   "intercept_us": round(my - slope * mx, 3),
+                   "intercept_us": round(intercept, 3),
                    "note": "decode site (T=1) from a HIP graph of 50 sites at each Sinkhorn "
                            "iteration count; slope = the Sinkhorn's cost per iteration, "
                            "intercept = everything else"}

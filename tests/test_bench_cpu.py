@@ -86,3 +86,18 @@ def test_traffic_is_dropped_when_the_kernel_sources_change(tmp_path, monkeypatch
                             bench.kernel_source_hash(bench.KERNEL_SOURCES["pre_call"])}},
               open(out, "w"))
     assert bench.load_traffic("pre_call") == 123
+
+
+def test_fit_line_matches_least_squares():
+    import numpy as np
+    xs = [1, 5, 10, 20, 40]
+    ys = [8.58, 8.71, 8.66, 9.32, 10.48]
+    slope, intercept = bench.fit_line(xs, ys)
+    want = np.polyfit(np.array(xs, float), np.array(ys, float), 1)
+    assert abs(slope - want[0]) < 1e-12 and abs(intercept - want[1]) < 1e-12
+    # an exact line is recovered exactly
+    assert bench.fit_line([0, 1, 2], [3.0, 5.0, 7.0]) == (2.0, 3.0)
+    with pytest.raises(ValueError):
+        bench.fit_line([1], [2.0])
+    with pytest.raises(ValueError):
+        bench.fit_line([2, 2], [1.0, 3.0])
