@@ -141,6 +141,40 @@ def time_site(mhc, torch, t, c, out_pre, out_x, steps, warmup):
     return start.elapsed_time(end) / steps, pre_ms, post_ms, wall, eager_ms
 
 
+def time_site_packed(mhc, torch, t, c, out_pre, out_x, steps):
+    """The timed steps of time_site with the site's weight packed once beforehand
+    (mhc_pack_weight, outside the timed region) and read by mhc_site_pre_packed:
+    K sites in one HIP graph, replayed once after one untimed replay.  Returns ms
+    per step, or None when the shape has no packed form."""
+    if mhc.packed_weight_bytes(c.S, c.H) == 0:
+        return None
+    packed = mhc.pack_weight(t["fn_w"], c.S, c.H)
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            mhc.site_pre(t["x"], t["fn_w"], t["scale"], t["base"], c.iters, c.eps, out=out_pre,
+                         packed=packed)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for _ in range(steps):
+            mhc.site_pre(t["x"], t["fn_w"], t["scale"], t["base"], c.iters, c.eps, out=out_pre,
+                         packed=packed)
+            mhc.site_post(t["x"], t["f"], out_pre[1], out_pre[2], out=out_x)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(side):
+        g.replay()
+        a.record(side)
+        g.replay()
+        b.record(side)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
 def time_decode(mhc, torch, t, c, out_pre, out_x, sites, graph_sites=50, zq8=None):
     """Decode sites back to back on one stream: (a) eager calls, no per-call events
     (host launch cost included); (b) a HIP graph of `graph_sites` sites replayed,
@@ -622,6 +656,7 @@ def main():
     out_pre, out_x = alloc_out(c.T, c.S, c.H, torch)
     ms, pre_ms, post_ms, wall, eager_ms = time_site(mhc, torch, t, c, out_pre, out_x,
                                                     args.steps, args.warmup)
+    packed_ms = time_site_packed(mhc, torch, t, c, out_pre, out_x, args.steps)
     pre_b, post_b = algorithmic_bytes(c.T, c.S, c.H)
     site_gbps = (pre_b + post_b) / (ms * 1e-3) / 1e9
     if post_ms >= pre_ms:
@@ -817,12 +852,19 @@ def main():
                      "frac_of_peak": round(site_gbps / PEAK_HBM_GBPS, 4),
                      "pre_us": round(pre_ms * 1e3, 2), "post_us": round(post_ms * 1e3, 2),
                      "eager_ms_per_step": round(eager_ms, 4),
+                     "packed_weight_ms_per_step": (round(packed_ms, 4) if packed_ms else None),
+                     "packed_weight_tokens_per_s": (round(c.T / (packed_ms * 1e-3), 1)
+                                                    if packed_ms else None),
+                     "packed_weight_GBps": (round((pre_b + post_b) / (packed_ms * 1e-3) / 1e9,
+                                                  1) if packed_ms else None),
                      "algorithmic_bytes_per_step": pre_b + post_b,
                      "note": "ms_per_step: the `steps` sites (pre + post each) captured in one "
                              "HIP graph and replayed once after one untimed replay, HIP events "
                              "around the replay; eager_ms_per_step: the same steps as plain "
                              "calls with an event between the calls, whose per-call times give "
-                             "pre_us and post_us"},
+                             "pre_us and post_us; packed_weight_*: the same timed steps with "
+                             "the site weight packed once beforehand (mhc_pack_weight) and read "
+                             "by mhc_site_pre_packed, as a trunk with fixed weights runs them"},
         "small_sites": verify,
         "decode_iters_sweep": iters_sweep,
         "decode_cold": cold,

@@ -109,6 +109,35 @@ int mhc_site_post(const float* x, const float* f, const float* post, const float
                   int T, int streams, int hidden, float* x_out, void* stream);
 
 /*
+ * Pre-packed mixes weight.  A site's weight fn_w is a fixed parameter (the
+ * hyper.rs page's module doc: the mixes weight of a site, [R][S*H]), while the
+ * large-batch pre kernel reads it in its own MFMA operand order, which
+ * mhc_site_pre produces by packing fn_w into the library scratch on every
+ * call.  A caller that keeps a site's weight can pack it once instead:
+ *
+ * mhc_packed_weight_bytes(streams, hidden): bytes of the packed form, or 0 for
+ *   a shape the large-batch kernel does not serve (then no packed form exists
+ *   and mhc_site_pre_packed takes packed == NULL).
+ * mhc_pack_weight(fn_w, streams, hidden, packed, stream): writes the packed
+ *   form of fn_w [R][S*H] into packed (mhc_packed_weight_bytes bytes, caller
+ *   owned, 16-byte aligned, not overlapping fn_w).  MHC_EUNSUPPORTED for a
+ *   shape with no packed form; asynchronous on `stream`.
+ * mhc_site_pre_packed(x, fn_w, packed, scale, base, ...): mhc_site_pre with
+ *   the weight read from `packed` wherever the large-batch kernel runs (fn_w
+ *   is still read on the small-batch path).  packed must hold
+ *   mhc_pack_weight's output for this fn_w and shape, and must not overlap the
+ *   outputs (MHC_EOVERLAP); NULL is MHC_EINVAL for a shape with a packed form.
+ *   The results are bit-identical to mhc_site_pre's.  Nothing is written to
+ *   the library scratch on the large-batch path.
+ */
+size_t mhc_packed_weight_bytes(int streams, int hidden);
+int mhc_pack_weight(const float* fn_w, int streams, int hidden, float* packed, void* stream);
+int mhc_site_pre_packed(const float* x, const float* fn_w, const float* packed,
+                        const float* scale, const float* base, int T, int streams, int hidden,
+                        int iters, float eps, float* pre, float* post, float* comb, float* y,
+                        void* stream);
+
+/*
  * mhc_site_pre_exact -- mhc_site_pre with decode-exact batching: every token's
  * pre, post, comb and y are bit-identical to those of a call of mhc_site_pre on
  * that token alone (T = 1), whatever T is and whatever else is in the batch

@@ -19,7 +19,8 @@ import os
 
 __all__ = ["site_pre", "site_post", "site_pre_zq8", "site_pre_check", "site_post_check",
            "site_pre_zq8_check", "site_post_pre", "site_post_pre_check", "expand", "mean",
-           "head", "head_check", "bandwidth_probe", "Workspace",
+           "head", "head_check", "bandwidth_probe", "packed_weight_bytes", "pack_weight",
+           "Workspace",
            "workspace_bytes", "load_library", "MhcError", "LIB_PATH", "EXPORTED_SYMBOLS",
            "STATUS"]
 
@@ -32,7 +33,8 @@ EXPORTED_SYMBOLS = ("mhc_site_pre", "mhc_site_post", "mhc_site_pre_exact", "mhc_
                     "mhc_ws_site_pre", "mhc_ws_site_pre_zq8", "mhc_ws_site_post",
                     "mhc_expand", "mhc_mean", "mhc_head", "mhc_head_check",
                     "mhc_site_post_pre", "mhc_site_post_pre_zq8", "mhc_site_post_pre_check",
-                    "mhc_status_string", "mhc_probe_sink_floats", "mhc_bandwidth_probe")
+                    "mhc_status_string", "mhc_probe_sink_floats", "mhc_bandwidth_probe",
+                    "mhc_packed_weight_bytes", "mhc_pack_weight", "mhc_site_pre_packed")
 
 STATUS = {0: "MHC_OK", 1: "MHC_EINVAL", 2: "MHC_EALIGN", 3: "MHC_EUNSUPPORTED",
           4: "MHC_EHIP", 5: "MHC_EOVERLAP"}
@@ -104,6 +106,12 @@ def load_library() -> ctypes.CDLL:
     lib.mhc_head.restype = i
     lib.mhc_head_check.argtypes = [vp, vp, vp, vp, i, i, i, fl, vp, vp]
     lib.mhc_head_check.restype = i
+    lib.mhc_packed_weight_bytes.argtypes = [i, i]
+    lib.mhc_packed_weight_bytes.restype = sz
+    lib.mhc_pack_weight.argtypes = [vp, i, i, vp, vp]
+    lib.mhc_pack_weight.restype = i
+    lib.mhc_site_pre_packed.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, fl, vp, vp, vp, vp, vp]
+    lib.mhc_site_pre_packed.restype = i
     lib.mhc_probe_sink_floats.argtypes = [sz]
     lib.mhc_probe_sink_floats.restype = sz
     lib.mhc_bandwidth_probe.argtypes = [vp, vp, sz, i, vp]
@@ -147,10 +155,13 @@ def _stream_handle(stream):
 
 
 def site_pre(x, fn_w, scale, base, iters: int, eps: float, *, out=None, stream=None,
-             exact: bool = False):
+             exact: bool = False, packed=None):
     """Pre half of a site.  x: [T,S,H]; fn_w: [(2+S)*S, S*H]; scale: [3]; base: [(2+S)*S].
     Returns (pre [T,S], post [T,S], comb [T,S,S], y [T,H]); `out` may supply that tuple.
-    exact=True calls mhc_site_pre_exact (every row bit-identical to a solo T=1 call)."""
+    exact=True calls mhc_site_pre_exact (every row bit-identical to a solo T=1 call);
+    packed (from pack_weight) calls mhc_site_pre_packed (same results, no per-call pack)."""
+    if exact and packed is not None:
+        raise ValueError("exact and packed are separate calls")
     import torch
     lib = load_library()
     if x.dim() != 3:
@@ -169,11 +180,43 @@ def site_pre(x, fn_w, scale, base, iters: int, eps: float, *, out=None, stream=N
     pre, post, comb, y = out
     ptrs = (_dev(pre, "pre", (T, S)), _dev(post, "post", (T, S)),
             _dev(comb, "comb", (T, S, S)), _dev(y, "y", (T, H)))
+    if packed is not None:
+        nbytes = int(lib.mhc_packed_weight_bytes(S, H))
+        pk = _dev(packed, "packed", (nbytes // 4,)) if nbytes else None
+        rc = lib.mhc_site_pre_packed(px, pw, pk, ps, pb, T, S, H, int(iters), float(eps), *ptrs,
+                                     _stream_handle(stream))
+        if rc != 0:
+            raise MhcError("mhc_site_pre_packed", rc, _status_text(lib, rc))
+        return out
     fn, name = ((lib.mhc_site_pre_exact, "mhc_site_pre_exact") if exact
                 else (lib.mhc_site_pre, "mhc_site_pre"))
     rc = fn(px, pw, ps, pb, T, S, H, int(iters), float(eps), *ptrs, _stream_handle(stream))
     if rc != 0:
         raise MhcError(name, rc, _status_text(lib, rc))
+    return out
+
+
+def packed_weight_bytes(streams: int, hidden: int) -> int:
+    """Bytes of a site weight's packed form (0: the shape has none)."""
+    return int(load_library().mhc_packed_weight_bytes(streams, hidden))
+
+
+def pack_weight(fn_w, streams: int, hidden: int, *, out=None, stream=None):
+    """Pack a site weight fn_w [(2+S)*S, S*H] once for site_pre(..., packed=...).
+    Returns a float32 GPU tensor of packed_weight_bytes(S, H) / 4 floats."""
+    import torch
+    lib = load_library()
+    S, H = int(streams), int(hidden)
+    R = (2 + S) * S
+    nbytes = int(lib.mhc_packed_weight_bytes(S, H))
+    if nbytes == 0:
+        raise MhcError("mhc_pack_weight", 3, _status_text(lib, 3))
+    pw = _dev(fn_w, "fn_w", (R, S * H))
+    if out is None:
+        out = torch.empty(nbytes // 4, device=fn_w.device, dtype=torch.float32)
+    rc = lib.mhc_pack_weight(pw, S, H, _dev(out, "packed", (nbytes // 4,)), _stream_handle(stream))
+    if rc != 0:
+        raise MhcError("mhc_pack_weight", rc, _status_text(lib, rc))
     return out
 
 

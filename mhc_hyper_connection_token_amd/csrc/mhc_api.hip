@@ -228,17 +228,25 @@ namespace {
 int site_pre_run(const float* x, const float* fn_w, const float* scale, const float* base, int T,
                  int S, int H, int iters, float eps, float* pre, float* post, float* comb,
                  float* y, const mhc::Zq8Out* zq, hipStream_t st,
-                 const ScratchSource& src = ScratchSource()) {
+                 const ScratchSource& src = ScratchSource(), const float* packed = nullptr) {
   int rc;
   const int n = S * H, R = (2 + S) * S;
   bool zq_done = false;
   if (T >= kFusedMinTokens && mhc::fused_supported(S, H)) {
-    // Large batches with a slab that fits on chip: x read once.
-    Scratch sc;
-    if ((rc = acquire_scratch(src, mhc::fused_pack_bytes(S, H), &sc))) return rc;
-    if (mhc::launch_fused_pre(x, fn_w, scale, base, T, S, H, iters, eps, pre, post, comb, y,
-                              sc.general, zq, nullptr, st) != hipSuccess)
-      return MHC_EHIP;
+    // Large batches with a slab that fits on chip: x read once.  A weight the
+    // caller packed beforehand is read as it is; otherwise it is packed into
+    // the scratch first.
+    hipError_t e;
+    if (packed) {
+      e = mhc::launch_fused_pre(x, fn_w, scale, base, T, S, H, iters, eps, pre, post, comb, y,
+                                const_cast<float*>(packed), zq, nullptr, st, true);
+    } else {
+      Scratch sc;
+      if ((rc = acquire_scratch(src, mhc::fused_pack_bytes(S, H), &sc))) return rc;
+      e = mhc::launch_fused_pre(x, fn_w, scale, base, T, S, H, iters, eps, pre, post, comb, y,
+                                sc.general, zq, nullptr, st);
+    }
+    if (e != hipSuccess) return MHC_EHIP;
     zq_done = true;
   } else {
     const PrePlan p = plan_split(T, S, H);
@@ -303,6 +311,50 @@ int mhc_site_pre(const float* x, const float* fn_w, const float* scale, const fl
   if (rc || T == 0) return rc;
   return site_pre_run(x, fn_w, scale, base, T, streams, hidden, iters, eps, pre, post, comb, y,
                       nullptr, static_cast<hipStream_t>(stream));
+}
+
+size_t mhc_packed_weight_bytes(int streams, int hidden) {
+  if (streams < 1 || hidden < 1 || hidden % 4 != 0 || !mhc::fused_supported(streams, hidden))
+    return 0;
+  return mhc::fused_pack_bytes(streams, hidden);
+}
+
+int mhc_pack_weight(const float* fn_w, int streams, int hidden, float* packed, void* stream) {
+  int rc = check_shape(1, streams, hidden);
+  if (rc) return rc;
+  const size_t pb = mhc_packed_weight_bytes(streams, hidden);
+  if (pb == 0) return MHC_EUNSUPPORTED;
+  if (!fn_w || !packed) return MHC_EINVAL;
+  if ((rc = check_ptr(fn_w)) || (rc = check_ptr(packed))) return rc;
+  const size_t R = (2 + streams) * streams, n = (size_t)streams * hidden;
+  if (overlaps(span(packed, pb), span(fn_w, R * n * 4))) return MHC_EOVERLAP;
+  return mhc::launch_pack_weight(fn_w, streams, hidden, packed,
+                                 static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MHC_OK
+             : MHC_EHIP;
+}
+
+int mhc_site_pre_packed(const float* x, const float* fn_w, const float* packed,
+                        const float* scale, const float* base, int T, int streams, int hidden,
+                        int iters, float eps, float* pre, float* post, float* comb, float* y,
+                        void* stream) {
+  int rc = mhc_site_pre_check(x, fn_w, scale, base, T, streams, hidden, iters, eps, pre, post,
+                              comb, y);
+  if (rc || T == 0) return rc;
+  const size_t pb = mhc_packed_weight_bytes(streams, hidden);
+  if (pb) {
+    if (!packed) return MHC_EINVAL;
+    if ((rc = check_ptr(packed))) return rc;
+    const size_t S = streams, H = hidden, Tz = T;
+    const Span p = span(packed, pb);
+    const Span out[] = {span(pre, Tz * S * 4), span(post, Tz * S * 4),
+                        span(comb, Tz * S * S * 4), span(y, Tz * H * 4)};
+    for (const Span& o : out)
+      if (overlaps(o, p)) return MHC_EOVERLAP;
+  }
+  return site_pre_run(x, fn_w, scale, base, T, streams, hidden, iters, eps, pre, post, comb, y,
+                      nullptr, static_cast<hipStream_t>(stream), ScratchSource(),
+                      pb ? packed : nullptr);
 }
 
 int mhc_site_pre_exact(const float* x, const float* fn_w, const float* scale, const float* base,

@@ -345,10 +345,30 @@ size_t fused_pack_bytes(int S, int H) { return pack_bytes_rows(S, (2 + S) * S, H
 
 size_t fused_head_pack_bytes(int S, int H) { return pack_bytes_rows(S, S, H); }
 
+hipError_t launch_pack_weight(const float* fn_w, int S, int H, float* wpack, hipStream_t st) {
+  if (!fused_supported(S, H)) return hipErrorInvalidValue;
+  const int cpw = fused_cpw(H);
+  const int total = (int)(fused_pack_bytes(S, H) / sizeof(float4));
+  float4* pk = reinterpret_cast<float4*>(wpack);
+#define MHC_PK(SS, CC)                                                                        \
+  if (S == SS && cpw == CC) {                                                                 \
+    hipLaunchKernelGGL((pack_weight_kernel<SS, (2 + SS) * SS, CC>), dim3((total + 255) / 256), \
+                       dim3(256), 0, st, fn_w, H, pk);                                        \
+    return hipGetLastError();                                                                 \
+  }
+  MHC_PK(1, 1) MHC_PK(1, 2) MHC_PK(1, 4) MHC_PK(1, 8) MHC_PK(1, 16)
+  MHC_PK(2, 1) MHC_PK(2, 2) MHC_PK(2, 4) MHC_PK(2, 8) MHC_PK(2, 16)
+  MHC_PK(3, 1) MHC_PK(3, 2) MHC_PK(3, 4) MHC_PK(3, 8)
+  MHC_PK(4, 1) MHC_PK(4, 2) MHC_PK(4, 4) MHC_PK(4, 8)
+#undef MHC_PK
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_fused_pre(const float* x, const float* fn_w, const float* scale,
                             const float* base, int T, int S, int H, int iters, float eps,
                             float* pre, float* post, float* comb, float* y, float* wpack,
-                            const Zq8Out* zq, const PostIn* pin, hipStream_t st) {
+                            const Zq8Out* zq, const PostIn* pin, hipStream_t st,
+                            bool prepacked) {
   if (!fused_supported(S, H) || (zq && H % 32 != 0)) return hipErrorInvalidValue;
   const Zq8Out zv = zq ? *zq : Zq8Out{nullptr, 0.f, nullptr, nullptr, nullptr};
   const PostIn pv = pin ? *pin : PostIn{nullptr, nullptr, nullptr, nullptr};
@@ -361,8 +381,9 @@ hipError_t launch_fused_pre(const float* x, const float* fn_w, const float* scal
                      base, T, H, iters, eps, pre, post, comb, y, zv, pv)
 #define MHC_FU(SS, CC)                                                                        \
   if (S == SS && cpw == CC) {                                                                 \
-    hipLaunchKernelGGL((pack_weight_kernel<SS, (2 + SS) * SS, CC>), dim3((total + 255) / 256), \
-                       dim3(256), 0, st, fn_w, H, pk);                                        \
+    if (!prepacked)                                                                           \
+      hipLaunchKernelGGL((pack_weight_kernel<SS, (2 + SS) * SS, CC>),                         \
+                         dim3((total + 255) / 256), dim3(256), 0, st, fn_w, H, pk);           \
     if (pin) {                                                                                \
       if (zq)                                                                                 \
         MHC_FK(SS, CC, true, true);                                                           \

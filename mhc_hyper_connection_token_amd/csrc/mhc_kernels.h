@@ -45,15 +45,19 @@ struct PostIn {
 
 // Token-tiled fused pre chain (slab held on chip), for S <= 4 and H up to a
 // register budget; fused_supported() says whether a shape qualifies.
-// wpack: scratch of fused_pack_bytes(S, H) bytes for the weight in operand order.
+// wpack: scratch of fused_pack_bytes(S, H) bytes for the weight in operand order,
+// filled by the call; with prepacked, wpack already holds launch_pack_weight's
+// output for fn_w and is only read.
 // With zq non-null (H % 32 == 0) the kernel also writes the branch-input epilogue;
 // with pin non-null it first runs the previous site's post mix on x.
 bool fused_supported(int S, int H);
 size_t fused_pack_bytes(int S, int H);
+hipError_t launch_pack_weight(const float* fn_w, int S, int H, float* wpack, hipStream_t st);
 hipError_t launch_fused_pre(const float* x, const float* fn_w, const float* scale,
                             const float* base, int T, int S, int H, int iters, float eps,
                             float* pre, float* post, float* comb, float* y, float* wpack,
-                            const Zq8Out* zq, const PostIn* pin, hipStream_t st);
+                            const Zq8Out* zq, const PostIn* pin, hipStream_t st,
+                            bool prepacked = false);
 
 // The gated head (R = S rows, one scale, S biases, sigmoid gates, collapse) on
 // the same token tiles, for the shapes fused_supported() accepts; wpack holds

@@ -283,3 +283,26 @@ def test_bandwidth_probe_refuses_before_any_gpu_work(lib):
     assert lib.mhc_bandwidth_probe(vp(a), vp(a + 32), 64, 1, None) == EOVERLAP
     assert lib.mhc_probe_sink_floats(1 << 20) == (1 << 20) // 4096
     assert lib.mhc_probe_sink_floats(16) == 1
+
+
+def test_packed_weight_calls_refuse_before_any_gpu_work(lib):
+    vp = ctypes.c_void_p
+    # a shape the large-batch kernel serves has a packed form; S > 4 has none
+    assert lib.mhc_packed_weight_bytes(4, 4096) == 8 * 4 * 8 * 6 * 64 * 16
+    assert lib.mhc_packed_weight_bytes(8, 7168) == 0
+    assert lib.mhc_packed_weight_bytes(4, 6) == 0
+    a, b = 4096, 4096 + (64 << 20)
+    assert lib.mhc_pack_weight(vp(a), 8, 7168, vp(b), None) == EUNSUP
+    assert lib.mhc_pack_weight(None, 4, 4096, vp(b), None) == EINVAL
+    assert lib.mhc_pack_weight(vp(a), 4, 4096, vp(b + 4), None) == EALIGN
+    assert lib.mhc_pack_weight(vp(a), 4, 4096, vp(a + 64), None) == EOVERLAP
+    # the pre call with a packed form: NULL refused, outputs may not overlap it
+    base_addr = 1 << 30
+    step = 1 << 26
+    x, w, sc, bs, pk, o1, o2, o3, o4 = (vp(base_addr + k * step) for k in range(9))
+    assert pk.value and lib.mhc_site_pre_packed(x, w, None, sc, bs, 300, 4, 4096, 20, ctypes.c_float(1e-6),
+                                   o1, o2, o3, o4, None) == EINVAL
+    assert lib.mhc_site_pre_packed(x, w, o4, sc, bs, 300, 4, 4096, 20, ctypes.c_float(1e-6),
+                                   o1, o2, o3, o4, None) == EOVERLAP
+    assert lib.mhc_site_pre_packed(x, w, vp(base_addr + 4 * step + 4), sc, bs, 300, 4, 4096, 20,
+                                   ctypes.c_float(1e-6), o1, o2, o3, o4, None) == EALIGN
