@@ -428,10 +428,28 @@ def time_walk(mhc, torch, c, x0, L, steps, warmup):
             x, o = xn, on
         mhc.site_post(x, sites[-1]["f"], o[1], o[2], out=xs[1 + L % 2])
 
+    packs = ([mhc.pack_weight(st["fn_w"], S, H) for st in sites]
+             if mhc.packed_weight_bytes(S, H) else None)
+
+    def fused_packed():
+        o = gates[0]
+        mhc.site_pre(xs[0], sites[0]["fn_w"], sites[0]["scale"], sites[0]["base"], c.iters,
+                     c.eps, out=o, packed=packs[0])
+        x = xs[0]
+        for k in range(1, L):
+            st, prev = sites[k], sites[k - 1]
+            on = gates[k % 2]
+            xn = xs[1 + k % 2]
+            mhc.site_post_pre(x, prev["f"], o[1], o[2], st["fn_w"], st["scale"], st["base"],
+                              c.iters, c.eps, out=(xn,) + tuple(on), packed=packs[k])
+            x, o = xn, on
+        mhc.site_post(x, sites[-1]["f"], o[1], o[2], out=xs[1 + L % 2])
+
     return (time_calls(torch, separate, steps, warmup) / L,
             time_calls(torch, fused, steps, warmup) / L,
             time_graph(torch, separate, calls=4, reps=3) / L,
-            time_graph(torch, fused, calls=4, reps=3) / L)
+            time_graph(torch, fused, calls=4, reps=3) / L,
+            (time_graph(torch, fused_packed, calls=4, reps=3) / L) if packs else None)
 
 
 def time_decode_walk(mhc, torch, c, x0, L=50, zq8=False, distinct=4):
@@ -770,7 +788,7 @@ def main():
     epi_us = zq_pre_us - pre_ms * 1e3
 
     # ---- a walk over 8 sites: separate calls against the fused post-then-pre schedule
-    walk_sep_us, walk_fused_us, walk_sep_g_us, walk_fused_g_us = time_walk(
+    walk_sep_us, walk_fused_us, walk_sep_g_us, walk_fused_g_us, walk_packed_g_us = time_walk(
         mhc, torch, c, t["x"], 8, max(3, args.steps // 5), 2)
     walk_traffic = load_traffic("walk_call")
     walk = {"sites": 8,
@@ -778,6 +796,10 @@ def main():
             "fused_us_per_site": round(walk_fused_us, 2),
             "separate_graph_us_per_site": round(walk_sep_g_us, 2),
             "fused_graph_us_per_site": round(walk_fused_g_us, 2),
+            "fused_packed_weight_graph_us_per_site": (round(walk_packed_g_us, 2)
+                                                      if walk_packed_g_us else None),
+            "fused_packed_weight_tokens_per_s": (round(c.T / (walk_packed_g_us * 1e-6), 1)
+                                                 if walk_packed_g_us else None),
             "fused_tokens_per_s": round(c.T / (walk_fused_g_us * 1e-6), 1),
             "fused_equivalent_GBps": round((pre_b + post_b) / (walk_fused_g_us * 1e-6) / 1e9, 1),
             "fused_call_traffic": walk_traffic,
@@ -787,7 +809,8 @@ def main():
                     "and the next site's pre in one kernel (mhc_site_post_pre), bit-identical "
                     "to the separate calls.  *_us_per_site: eager walks with HIP events; "
                     "*_graph_us_per_site: 4 walks captured in one HIP graph, replayed; the "
-                    "rates use the graph figure.  equivalent_GBps counts one pre + post's "
+                    "rates use the graph figure; fused_packed_weight: every site weight packed "
+                    "once beforehand (mhc_pack_weight), the walk reading the packed copies.  equivalent_GBps counts one pre + post's "
                     "algorithmic bytes (the fused call does not re-read the new state); "
                     "traffic_GBps is the measured HBM bytes of the fused call (pack + kernel) "
                     "per site time"}

@@ -136,6 +136,15 @@ int mhc_site_pre_packed(const float* x, const float* fn_w, const float* packed,
                         const float* scale, const float* base, int T, int streams, int hidden,
                         int iters, float eps, float* pre, float* post, float* comb, float* y,
                         void* stream);
+/* mhc_site_post_pre with the next site's weight read from `packed` wherever the
+ * fused kernel runs: same arguments as mhc_site_post_pre plus `packed`, with the
+ * conditions of mhc_site_pre_packed (packed must not overlap x_out or the
+ * outputs either); bit-identical results. */
+int mhc_site_post_pre_packed(const float* x, const float* f, const float* post_in,
+                             const float* comb_in, const float* fn_w, const float* packed,
+                             const float* scale, const float* base, int T, int streams,
+                             int hidden, int iters, float eps, float* x_out, float* pre,
+                             float* post, float* comb, float* y, void* stream);
 
 /*
  * mhc_site_pre_exact -- mhc_site_pre with decode-exact batching: every token's

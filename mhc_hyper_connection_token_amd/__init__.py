@@ -34,7 +34,8 @@ EXPORTED_SYMBOLS = ("mhc_site_pre", "mhc_site_post", "mhc_site_pre_exact", "mhc_
                     "mhc_expand", "mhc_mean", "mhc_head", "mhc_head_check",
                     "mhc_site_post_pre", "mhc_site_post_pre_zq8", "mhc_site_post_pre_check",
                     "mhc_status_string", "mhc_probe_sink_floats", "mhc_bandwidth_probe",
-                    "mhc_packed_weight_bytes", "mhc_pack_weight", "mhc_site_pre_packed")
+                    "mhc_packed_weight_bytes", "mhc_pack_weight", "mhc_site_pre_packed",
+                    "mhc_site_post_pre_packed")
 
 STATUS = {0: "MHC_OK", 1: "MHC_EINVAL", 2: "MHC_EALIGN", 3: "MHC_EUNSUPPORTED",
           4: "MHC_EHIP", 5: "MHC_EOVERLAP"}
@@ -112,6 +113,9 @@ def load_library() -> ctypes.CDLL:
     lib.mhc_pack_weight.restype = i
     lib.mhc_site_pre_packed.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, fl, vp, vp, vp, vp, vp]
     lib.mhc_site_pre_packed.restype = i
+    lib.mhc_site_post_pre_packed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, fl, vp,
+                                             vp, vp, vp, vp, vp]
+    lib.mhc_site_post_pre_packed.restype = i
     lib.mhc_probe_sink_floats.argtypes = [sz]
     lib.mhc_probe_sink_floats.restype = sz
     lib.mhc_bandwidth_probe.argtypes = [vp, vp, sz, i, vp]
@@ -294,11 +298,14 @@ def site_pre_zq8_check(x_ptr, fn_w_ptr, scale_ptr, base_ptr, nw_ptr, T, S, H, it
 
 
 def site_post_pre(x, f, post, comb, fn_w, scale, base, iters: int, eps: float, *, nw=None,
-                  norm_eps: float = 1e-5, out=None, stream=None):
+                  norm_eps: float = 1e-5, out=None, stream=None, packed=None):
     """The post half of a site (x, f, post, comb) followed by the pre half of the
     next site (fn_w, scale, base) on its output.  Returns (x_out, pre, post, comb, y),
     plus (z, q, d) when the norm weight nw of the next site's epilogue is given;
-    `out` may supply that tuple."""
+    `out` may supply that tuple.  packed (from pack_weight, without nw) calls
+    mhc_site_post_pre_packed."""
+    if packed is not None and nw is not None:
+        raise ValueError("the packed call has no epilogue")
     import torch
     lib = load_library()
     if x.dim() != 3:
@@ -321,7 +328,13 @@ def site_post_pre(x, f, post, comb, fn_w, scale, base, iters: int, eps: float, *
             _dev(out[2], "post", (T, S)), _dev(out[3], "comb", (T, S, S)),
             _dev(out[4], "y", (T, H))]
     st = _stream_handle(stream)
-    if nw is None:
+    if packed is not None:
+        nbytes = int(lib.mhc_packed_weight_bytes(S, H))
+        pk = _dev(packed, "packed", (nbytes // 4,)) if nbytes else None
+        rc = lib.mhc_site_post_pre_packed(px, pf, ppi, pci, pw, pk, ps, pb, T, S, H, int(iters),
+                                          float(eps), *ptrs, st)
+        name = "mhc_site_post_pre_packed"
+    elif nw is None:
         rc = lib.mhc_site_post_pre(px, pf, ppi, pci, pw, ps, pb, T, S, H, int(iters),
                                    float(eps), *ptrs, st)
         name = "mhc_site_post_pre"

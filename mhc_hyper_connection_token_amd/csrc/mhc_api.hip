@@ -284,19 +284,39 @@ int site_pre_run(const float* x, const float* fn_w, const float* scale, const fl
 int site_post_pre_run(const float* x, const float* f, const float* post_in, const float* comb_in,
                       const float* fn_w, const float* scale, const float* base, int T, int S,
                       int H, int iters, float eps, float* x_out, float* pre, float* post,
-                      float* comb, float* y, const mhc::Zq8Out* zq, hipStream_t st) {
+                      float* comb, float* y, const mhc::Zq8Out* zq, hipStream_t st,
+                      const float* packed = nullptr) {
   if (T >= kFusedMinTokens && mhc::fused_supported(S, H)) {
-    Scratch sc;
-    int rc;
-    if ((rc = get_scratch(mhc::fused_pack_bytes(S, H), &sc))) return rc;
     const mhc::PostIn pin{f, post_in, comb_in, x_out};
-    return mhc::launch_fused_pre(x, fn_w, scale, base, T, S, H, iters, eps, pre, post, comb, y,
-                                 sc.general, zq, &pin, st) == hipSuccess
-               ? MHC_OK
-               : MHC_EHIP;
+    hipError_t e;
+    if (packed) {
+      e = mhc::launch_fused_pre(x, fn_w, scale, base, T, S, H, iters, eps, pre, post, comb, y,
+                                const_cast<float*>(packed), zq, &pin, st, true);
+    } else {
+      Scratch sc;
+      int rc;
+      if ((rc = get_scratch(mhc::fused_pack_bytes(S, H), &sc))) return rc;
+      e = mhc::launch_fused_pre(x, fn_w, scale, base, T, S, H, iters, eps, pre, post, comb, y,
+                                sc.general, zq, &pin, st);
+    }
+    return e == hipSuccess ? MHC_OK : MHC_EHIP;
   }
   if (mhc::launch_post(x, f, post_in, comb_in, T, S, H, x_out, st) != hipSuccess) return MHC_EHIP;
-  return site_pre_run(x_out, fn_w, scale, base, T, S, H, iters, eps, pre, post, comb, y, zq, st);
+  return site_pre_run(x_out, fn_w, scale, base, T, S, H, iters, eps, pre, post, comb, y, zq, st,
+                      ScratchSource(), packed);
+}
+
+// A packed weight given with a call: checked against the shape and the outputs.
+int check_packed(const float* packed, int S, int H, const Span* outs, int nout, size_t* pb) {
+  *pb = mhc_packed_weight_bytes(S, H);
+  if (*pb == 0) return MHC_OK;
+  if (!packed) return MHC_EINVAL;
+  int rc;
+  if ((rc = check_ptr(packed))) return rc;
+  const Span p = span(packed, *pb);
+  for (int i = 0; i < nout; ++i)
+    if (overlaps(outs[i], p)) return MHC_EOVERLAP;
+  return MHC_OK;
 }
 
 }  // namespace
@@ -341,17 +361,11 @@ int mhc_site_pre_packed(const float* x, const float* fn_w, const float* packed,
   int rc = mhc_site_pre_check(x, fn_w, scale, base, T, streams, hidden, iters, eps, pre, post,
                               comb, y);
   if (rc || T == 0) return rc;
-  const size_t pb = mhc_packed_weight_bytes(streams, hidden);
-  if (pb) {
-    if (!packed) return MHC_EINVAL;
-    if ((rc = check_ptr(packed))) return rc;
-    const size_t S = streams, H = hidden, Tz = T;
-    const Span p = span(packed, pb);
-    const Span out[] = {span(pre, Tz * S * 4), span(post, Tz * S * 4),
-                        span(comb, Tz * S * S * 4), span(y, Tz * H * 4)};
-    for (const Span& o : out)
-      if (overlaps(o, p)) return MHC_EOVERLAP;
-  }
+  const size_t S = streams, H = hidden, Tz = T;
+  const Span out[] = {span(pre, Tz * S * 4), span(post, Tz * S * 4), span(comb, Tz * S * S * 4),
+                      span(y, Tz * H * 4)};
+  size_t pb;
+  if ((rc = check_packed(packed, streams, hidden, out, 4, &pb))) return rc;
   return site_pre_run(x, fn_w, scale, base, T, streams, hidden, iters, eps, pre, post, comb, y,
                       nullptr, static_cast<hipStream_t>(stream), ScratchSource(),
                       pb ? packed : nullptr);
@@ -474,6 +488,24 @@ int mhc_site_post_pre(const float* x, const float* f, const float* post_in, cons
   return site_post_pre_run(x, f, post_in, comb_in, fn_w, scale, base, T, streams, hidden, iters,
                            eps, x_out, pre, post, comb, y, nullptr,
                            static_cast<hipStream_t>(stream));
+}
+
+int mhc_site_post_pre_packed(const float* x, const float* f, const float* post_in,
+                             const float* comb_in, const float* fn_w, const float* packed,
+                             const float* scale, const float* base, int T, int streams,
+                             int hidden, int iters, float eps, float* x_out, float* pre,
+                             float* post, float* comb, float* y, void* stream) {
+  int rc = mhc_site_post_pre_check(x, f, post_in, comb_in, fn_w, scale, base, T, streams, hidden,
+                                   iters, eps, x_out, pre, post, comb, y);
+  if (rc || T == 0) return rc;
+  const size_t S = streams, H = hidden, Tz = T;
+  const Span out[] = {span(x_out, Tz * S * H * 4), span(pre, Tz * S * 4),
+                      span(post, Tz * S * 4), span(comb, Tz * S * S * 4), span(y, Tz * H * 4)};
+  size_t pb;
+  if ((rc = check_packed(packed, streams, hidden, out, 5, &pb))) return rc;
+  return site_post_pre_run(x, f, post_in, comb_in, fn_w, scale, base, T, streams, hidden, iters,
+                           eps, x_out, pre, post, comb, y, nullptr,
+                           static_cast<hipStream_t>(stream), pb ? packed : nullptr);
 }
 
 int mhc_site_post_pre_zq8(const float* x, const float* f, const float* post_in,

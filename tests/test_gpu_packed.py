@@ -53,3 +53,18 @@ def test_no_packed_form_for_wide_sites(mhc):
     d = {k: torch.from_numpy(v).cuda() for k, v in make_random_shape(T, S, H, seed=9).items()}
     with pytest.raises(mhc.MhcError):
         mhc.pack_weight(d["fn_w"], S, H)
+
+
+@pytest.mark.parametrize("T,S,H", [(2, 4, 4096), (300, 4, 4096), (4096, 4, 4096), (259, 3, 1028)])
+def test_packed_walk_equals_plain_walk(mhc, T, S, H):
+    print(f"[case] packed walk T={T} S={S} H={H}", flush=True)
+    a = {k: torch.from_numpy(v).cuda() for k, v in make_random_shape(T, S, H, seed=1).items()}
+    b = {k: torch.from_numpy(v).cuda() for k, v in make_random_shape(T, S, H, seed=2).items()}
+    p0, q0, c0, _ = mhc.site_pre(a["x"], a["fn_w"], a["scale"], a["base"], 20, 1e-6)
+    packed = mhc.pack_weight(b["fn_w"], S, H)
+    plain = mhc.site_post_pre(a["x"], a["f"], q0, c0, b["fn_w"], b["scale"], b["base"], 20, 1e-6)
+    pk = mhc.site_post_pre(a["x"], a["f"], q0, c0, b["fn_w"], b["scale"], b["base"], 20, 1e-6,
+                           packed=packed)
+    torch.cuda.synchronize()
+    for name, u, v in zip(("x_out", "pre", "post", "comb", "y"), plain, pk):
+        assert torch.equal(u, v), f"{name} differs between the packed and the plain walk"
