@@ -77,7 +77,9 @@ def _walk_fused(mhc, x0, sites, nw):
                                       (64, 4, 1024, False), (200, 4, 4096, False),
                                       (3, 4, 16384, False), (2, 2, 65536, False),
                                       (3, 8, 512, False), (1, 4, 4096, True),
-                                      (257, 1, 8192, False)])
+                                      (257, 1, 8192, False),
+                                      # the prefill chunk and a ragged tile count
+                                      (4096, 4, 4096, False), (1001, 3, 2048, True)])
 def test_fused_walk_equals_separate_calls(mhc, T, S, H, zq):
     print(f"[case] walk T{T} S{S} H{H} zq8={zq}", flush=True)
     L = 4
