@@ -24,7 +24,9 @@ def mhc():
 
 
 @pytest.mark.parametrize("T,S,H", [(1, 4, 4096), (300, 4, 4096), (4096, 4, 4096),
-                                   (261, 3, 1028), (257, 1, 8192), (300, 2, 4)])
+                                   (261, 3, 1028), (257, 1, 8192), (300, 2, 4),
+                                   # a hidden size with a partly padded last column block
+                                   (300, 4, 1056), (513, 4, 3000)])
 def test_packed_equals_plain(mhc, T, S, H):
     print(f"[case] packed T={T} S={S} H={H}", flush=True)
     d = {k: torch.from_numpy(v).cuda() for k, v in make_random_shape(T, S, H, seed=T + S).items()}
@@ -68,3 +70,15 @@ def test_packed_walk_equals_plain_walk(mhc, T, S, H):
     torch.cuda.synchronize()
     for name, u, v in zip(("x_out", "pre", "post", "comb", "y"), plain, pk):
         assert torch.equal(u, v), f"{name} differs between the packed and the plain walk"
+
+
+def test_packed_calls_with_zero_tokens(mhc):
+    S, H = 4, 4096
+    print("[case] packed T=0", flush=True)
+    w = torch.zeros(((2 + S) * S, S * H), device="cuda")
+    packed = mhc.pack_weight(w, S, H)
+    x = torch.empty((0, S, H), device="cuda")
+    out = mhc.site_pre(x, w, torch.ones(3, device="cuda"), torch.zeros(24, device="cuda"), 20,
+                       1e-6, packed=packed)
+    torch.cuda.synchronize()
+    assert out[3].shape == (0, H)
