@@ -24,15 +24,22 @@
  *  - Layout is token-major: x[T][S][H], element (t,k,i) at (t*S+k)*H+i, so one
  *    token's S*H slab is contiguous.  S = streams, H = hidden, R = (2+S)*S.
  *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
- *    work; they never synchronise the host.  Results are ready once the stream
- *    reaches the enqueued work.
+ *    work and do not wait for the device, except that a call which must grow
+ *    the library scratch (below) allocates device memory with hipMalloc.
+ *    Results are ready once the stream reaches the enqueued work.
  *  - Every argument check happens on the host BEFORE any GPU work is enqueued;
  *    a call that returns an error has enqueued nothing.
  *  - Calls on the same device share one library-owned scratch area (partial
- *    sums of the split reduction).  Two calls enqueued on DIFFERENT streams of
- *    the same device must not run concurrently; calls on one stream are always
- *    safe.  The scratch is allocated by the first call that needs it on each
- *    device (a one-time hipMalloc) and lives until the process ends.
+ *    sums of the split reduction, the packed weight of the large-batch
+ *    kernel).  Two calls enqueued on DIFFERENT streams of the same device must
+ *    not run concurrently; calls on one stream are always safe.  The first
+ *    call on a device that needs scratch allocates it, and a later call that
+ *    needs more allocates a larger area (clearing its 256-byte header with
+ *    hipMemsetAsync on that call's stream).  No scratch area is ever freed
+ *    before the process ends, so HIP graphs captured earlier stay valid.  A
+ *    call that would have to grow the scratch while its stream is being
+ *    captured returns MHC_ECAPTURE: make one call of the largest size before
+ *    capturing (or use a workspace, which never allocates).
  *  - Supported shapes: 1 <= S <= 8, H >= 4 with H % 4 == 0, T >= 0
  *    (T == 0 is a no-op), iters >= 1, eps > 0 and finite, T*S*H < 2^31.
  *  - Numeric domain: finite inputs with |scale*m + base| below about 80, so
@@ -54,7 +61,8 @@ enum {
   MHC_EALIGN = 2,      /* H % 4 != 0 or a pointer not 16-byte aligned            */
   MHC_EUNSUPPORTED = 3,/* valid arguments the library does not handle (S > 8, sizes too large) */
   MHC_EHIP = 4,        /* the HIP runtime reported an error (launch, allocation) */
-  MHC_EOVERLAP = 5     /* an output buffer overlaps an input buffer              */
+  MHC_EOVERLAP = 5,    /* an output buffer overlaps an input buffer              */
+  MHC_ECAPTURE = 6     /* the scratch would have to grow while the stream is captured */
 };
 
 /*
@@ -88,6 +96,16 @@ enum {
 int mhc_site_pre(const float* x, const float* fn_w, const float* scale, const float* base,
                  int T, int streams, int hidden, int iters, float eps,
                  float* pre, float* post, float* comb, float* y, void* stream);
+
+/*
+ * mhc_site_pre_scratch_bytes -- bytes of library scratch (header included) that
+ * mhc_site_pre needs for T tokens of this shape: the packed weight where the
+ * large-batch kernel runs, else the split reduction's partial sums.  0 for
+ * T < 1 or a shape the call rejects.  Host only: no HIP call, safe without a
+ * GPU.  A caller that captures HIP graphs can make one eager call at its
+ * largest T first, or compare this figure across the shapes it will capture.
+ */
+size_t mhc_site_pre_scratch_bytes(int T, int streams, int hidden);
 
 /*
  * mhc_site_post -- the post half of one site (hyper.rs, doc comment of `post`):

@@ -20,6 +20,7 @@ import os
 __all__ = ["site_pre", "site_post", "site_pre_zq8", "site_pre_check", "site_post_check",
            "site_pre_zq8_check", "site_post_pre", "site_post_pre_check", "expand", "mean",
            "head", "head_check", "bandwidth_probe", "packed_weight_bytes", "pack_weight",
+           "site_pre_scratch_bytes",
            "Workspace",
            "workspace_bytes", "load_library", "MhcError", "LIB_PATH", "EXPORTED_SYMBOLS",
            "STATUS"]
@@ -35,10 +36,10 @@ EXPORTED_SYMBOLS = ("mhc_site_pre", "mhc_site_post", "mhc_site_pre_exact", "mhc_
                     "mhc_site_post_pre", "mhc_site_post_pre_zq8", "mhc_site_post_pre_check",
                     "mhc_status_string", "mhc_probe_sink_floats", "mhc_bandwidth_probe",
                     "mhc_packed_weight_bytes", "mhc_pack_weight", "mhc_site_pre_packed",
-                    "mhc_site_post_pre_packed")
+                    "mhc_site_post_pre_packed", "mhc_site_pre_scratch_bytes")
 
 STATUS = {0: "MHC_OK", 1: "MHC_EINVAL", 2: "MHC_EALIGN", 3: "MHC_EUNSUPPORTED",
-          4: "MHC_EHIP", 5: "MHC_EOVERLAP"}
+          4: "MHC_EHIP", 5: "MHC_EOVERLAP", 6: "MHC_ECAPTURE"}
 
 _lib = None
 
@@ -116,6 +117,8 @@ def load_library() -> ctypes.CDLL:
     lib.mhc_site_post_pre_packed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, fl, vp,
                                              vp, vp, vp, vp, vp]
     lib.mhc_site_post_pre_packed.restype = i
+    lib.mhc_site_pre_scratch_bytes.argtypes = [i, i, i]
+    lib.mhc_site_pre_scratch_bytes.restype = sz
     lib.mhc_probe_sink_floats.argtypes = [sz]
     lib.mhc_probe_sink_floats.restype = sz
     lib.mhc_bandwidth_probe.argtypes = [vp, vp, sz, i, vp]
@@ -198,6 +201,11 @@ def site_pre(x, fn_w, scale, base, iters: int, eps: float, *, out=None, stream=N
     if rc != 0:
         raise MhcError(name, rc, _status_text(lib, rc))
     return out
+
+
+def site_pre_scratch_bytes(T: int, streams: int, hidden: int) -> int:
+    """Bytes of library scratch a site_pre call of this shape needs (0: rejected shape)."""
+    return int(load_library().mhc_site_pre_scratch_bytes(T, streams, hidden))
 
 
 def packed_weight_bytes(streams: int, hidden: int) -> int:

@@ -38,12 +38,19 @@ int check_shape(int T, int S, int H) {
   return MHC_OK;
 }
 
-// Library-owned scratch, one buffer per device, grown on demand.  Its first
-// kScratchHeader bytes hold the decode kernels' ticket counter (zeroed when the
+// Library-owned scratch, one current buffer per device.  Its first
+// kScratchHeader bytes hold the decode kernels' ticket counter (cleared when the
 // buffer is allocated; the kernels leave it at zero); the rest is returned to
-// the caller (split-K partials, packed weight).  Growth waits for the device
-// to go idle before the old buffer is released, so work already enqueued that
-// still uses it is not disturbed.
+// the caller (split-K partials, packed weight).
+//
+// A call that needs more than the current buffer allocates a larger one and
+// makes it current.  The smaller one is never freed: work already enqueued on
+// it, and HIP graphs captured while it was current, keep pointing at valid
+// memory until the process ends (the buffers grow by a quarter each time, so
+// the retired ones add up to a bounded multiple of the largest).  Growth is a
+// hipMalloc, which HIP graph capture does not allow, so a call that would grow
+// the buffer while its stream is being captured returns MHC_ECAPTURE and
+// enqueues nothing; one call of the same size outside the capture sizes it.
 constexpr size_t kScratchHeader = 256;
 struct DeviceScratch {
   void* ptr = nullptr;
@@ -57,26 +64,29 @@ struct Scratch {
   unsigned int* counter = nullptr;
 };
 
-int get_scratch(size_t bytes, Scratch* out) {
+// Bytes of the next buffer when `need` bytes (header included) are wanted and
+// `have` are current: 1 MiB at least, then a quarter more than asked for.
+size_t scratch_grow_bytes(size_t need, size_t have) {
+  if (need <= have) return have;
+  return need < (size_t(1) << 20) ? (size_t(1) << 20) : need + need / 4;
+}
+
+int get_scratch(size_t bytes, hipStream_t st, Scratch* out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MHC_EHIP;
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   DeviceScratch& s = g_scratch[dev];
   const size_t need = bytes + kScratchHeader;
   if (s.bytes < need) {
-    size_t want = need < (size_t(1) << 20) ? (size_t(1) << 20) : need + need / 4;
-    if (s.ptr) {
-      if (hipDeviceSynchronize() != hipSuccess) return MHC_EHIP;
-      if (hipFree(s.ptr) != hipSuccess) return MHC_EHIP;
-      s.ptr = nullptr;
-      s.bytes = 0;
-    }
-    if (hipMalloc(&s.ptr, want) != hipSuccess) {
-      s.ptr = nullptr;
-      return MHC_EHIP;
-    }
-    if (hipMemset(s.ptr, 0, kScratchHeader) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
-      return MHC_EHIP;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cap) != hipSuccess) return MHC_EHIP;
+    if (cap != hipStreamCaptureStatusNone) return MHC_ECAPTURE;
+    const size_t want = scratch_grow_bytes(need, s.bytes);
+    void* p = nullptr;
+    if (hipMalloc(&p, want) != hipSuccess) return MHC_EHIP;
+    // the ticket starts at zero, ordered before this call's kernels
+    if (hipMemsetAsync(p, 0, kScratchHeader, st) != hipSuccess) return MHC_EHIP;
+    s.ptr = p;  // the previous buffer stays allocated (see above)
     s.bytes = want;
   }
   char* base = static_cast<char*>(s.ptr);
@@ -93,13 +103,13 @@ struct ScratchSource {
   size_t bytes = 0;
 };
 
-int acquire_scratch(const ScratchSource& src, size_t bytes, Scratch* out) {
+int acquire_scratch(const ScratchSource& src, size_t bytes, hipStream_t st, Scratch* out) {
   if (src.fixed) {
     if (bytes > src.bytes) return MHC_EINVAL;
     *out = *src.fixed;
     return MHC_OK;
   }
-  return get_scratch(bytes, out);
+  return get_scratch(bytes, st, out);
 }
 
 // Split-K plan for the pre chain: token tiles of 16*ntt tokens, G K-ranges of
@@ -169,8 +179,16 @@ const char* mhc_status_string(int status) {
              "the call handles)";
     case MHC_EHIP: return "HIP runtime error";
     case MHC_EOVERLAP: return "an output buffer overlaps an input or another output";
+    case MHC_ECAPTURE:
+      return "the call needs a larger library scratch area while its stream is being captured "
+             "(make one call of this size before the capture)";
     default: return "unknown status";
   }
+}
+
+size_t mhc_site_pre_scratch_bytes(int T, int streams, int hidden) {
+  if (T < 1 || check_shape(T, streams, hidden) != MHC_OK) return 0;
+  return kScratchHeader + pre_scratch_bytes(T, streams, hidden);
 }
 
 int mhc_site_pre_check(const float* x, const float* fn_w, const float* scale, const float* base,
@@ -242,7 +260,7 @@ int site_pre_run(const float* x, const float* fn_w, const float* scale, const fl
                                 const_cast<float*>(packed), zq, nullptr, st, true);
     } else {
       Scratch sc;
-      if ((rc = acquire_scratch(src, mhc::fused_pack_bytes(S, H), &sc))) return rc;
+      if ((rc = acquire_scratch(src, mhc::fused_pack_bytes(S, H), st, &sc))) return rc;
       e = mhc::launch_fused_pre(x, fn_w, scale, base, T, S, H, iters, eps, pre, post, comb, y,
                                 sc.general, zq, nullptr, st);
     }
@@ -251,7 +269,7 @@ int site_pre_run(const float* x, const float* fn_w, const float* scale, const fl
   } else {
     const PrePlan p = plan_split(T, S, H);
     Scratch sc;
-    if ((rc = acquire_scratch(src, p.part_floats * sizeof(float), &sc))) return rc;
+    if ((rc = acquire_scratch(src, p.part_floats * sizeof(float), st, &sc))) return rc;
     float* part = sc.general;
     hipError_t e;
     if (zq && mhc::decode_zq8_supported(T, S, H, p.G)) {
@@ -295,12 +313,17 @@ int site_post_pre_run(const float* x, const float* f, const float* post_in, cons
     } else {
       Scratch sc;
       int rc;
-      if ((rc = get_scratch(mhc::fused_pack_bytes(S, H), &sc))) return rc;
+      if ((rc = get_scratch(mhc::fused_pack_bytes(S, H), st, &sc))) return rc;
       e = mhc::launch_fused_pre(x, fn_w, scale, base, T, S, H, iters, eps, pre, post, comb, y,
                                 sc.general, zq, &pin, st);
     }
     return e == hipSuccess ? MHC_OK : MHC_EHIP;
   }
+  // size the scratch of the pre chain first, so that a refusal (MHC_ECAPTURE)
+  // comes before anything is enqueued
+  Scratch sc;
+  int rc;
+  if ((rc = get_scratch(pre_scratch_bytes(T, S, H), st, &sc))) return rc;
   if (mhc::launch_post(x, f, post_in, comb_in, T, S, H, x_out, st) != hipSuccess) return MHC_EHIP;
   return site_pre_run(x_out, fn_w, scale, base, T, S, H, iters, eps, pre, post, comb, y, zq, st,
                       ScratchSource(), packed);
@@ -390,7 +413,7 @@ int mhc_site_pre_exact(const float* x, const float* fn_w, const float* scale, co
   const PrePlan p1 = plan_pre(1, S, H);
   const int chunk = T < kExactChunk ? T : kExactChunk;
   Scratch sc;
-  if ((rc = get_scratch((size_t)p1.G * chunk * (R + 1) * sizeof(float), &sc))) return rc;
+  if ((rc = get_scratch((size_t)p1.G * chunk * (R + 1) * sizeof(float), st, &sc))) return rc;
   for (int t0 = 0; t0 < T; t0 += chunk) {
     const int tc = T - t0 < chunk ? T - t0 : chunk;
     const float* xc = x + (size_t)t0 * n;
@@ -629,7 +652,7 @@ int mhc_head(const float* x, const float* fn_w, const float* scale, const float*
     // Large batches with a slab that fits on chip: the site's token tiles with the
     // head's S rows, x read once.
     Scratch sc;
-    if ((rc = get_scratch(mhc::fused_head_pack_bytes(S, H), &sc))) return rc;
+    if ((rc = get_scratch(mhc::fused_head_pack_bytes(S, H), st, &sc))) return rc;
     return mhc::launch_fused_head(x, fn_w, scale, base, T, S, H, eps, gates, y, sc.general,
                                   st) == hipSuccess
                ? MHC_OK
@@ -640,7 +663,7 @@ int mhc_head(const float* x, const float* fn_w, const float* scale, const float*
   const PrePlan p1 = plan_pre(1, S, H);
   const int chunk = T < kExactChunk ? T : kExactChunk;
   Scratch sc;
-  if ((rc = get_scratch((size_t)p1.G * chunk * (S + 1) * sizeof(float), &sc))) return rc;
+  if ((rc = get_scratch((size_t)p1.G * chunk * (S + 1) * sizeof(float), st, &sc))) return rc;
   for (int t0 = 0; t0 < T; t0 += chunk) {
     const int tc = T - t0 < chunk ? T - t0 : chunk;
     const float* xc = x + (size_t)t0 * n;

@@ -56,8 +56,12 @@ __global__ __launch_bounds__(256) void decode_zq8_kernel(
                          [=](size_t i, float v) { store_partial<true>(pg + i, v); });
   __builtin_amdgcn_s_waitcnt(0);  // this thread's stores are complete ...
   __syncthreads();                // ... and so are those of the whole block
+  // The ticket: a release of the block's partials (ordered before it by the
+  // barrier) and, for the block that draws the last ticket, an acquire of
+  // everyone else's, both at agent scope, so that the last block's loads below
+  // see every partial under the memory model and not only on this hardware.
   if (tid == 0)
-    is_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+    is_last = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
               (unsigned)(G - 1);
   __syncthreads();
   if (!is_last) return;

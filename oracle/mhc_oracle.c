@@ -314,7 +314,8 @@ int mhc_oracle_sinkhorn(const double *z, int S, int iters, double eps,
  *       embedding into each stream; the page calls the mean kernel its
  *       inverse, and the mean of S equal copies is the copy).
  *   O11 mean:   y[t,i] = (sum_k x[t,k,i]) / S, streams in ascending order.
- *   O12 gated head ("sigmoid-gated pre-only collapse"): the pre half of a site
+ *   O12 gated head (the head's gates are sigmoids, and it has only the pre
+ *       half: no post gates and no combination block): the pre half of a site
  *       with the head's own S rows, one scale and S biases:
  *         rinv = 1/sqrt(sum_i x[t,i]^2 / (S*H) + eps)          (as O1)
  *         m_c  = rinv * sum_i fn_h[c,i] * x[t,i]                c < S

@@ -1,11 +1,11 @@
 """Comparison rules shared by the GPU parity tests.
 
 Gates (pre, post, comb): element-wise |gpu - oracle| <= 1e-6 + 1e-5 * |oracle|.
-Streams (y, x'): the worst absolute difference relative to the reference's own
-scale, max|gpu - oracle| / max(max|oracle|, 1e-6) <= 2e-5, evaluated per token
-row (the measure defined by the `relative` helper of the docs.rs page
-"memra-engine 0.125.0 src/bin/glm5_prime_v2_gate.rs").  Every output must be
-finite.
+Streams (y, x'): max|gpu - oracle| / max(max|oracle|, 1e-6) <= 2e-5, evaluated
+per token row: the largest error divided by the largest magnitude of the
+expected row, floored at 1e-6 (the measure of the `relative` helper on the
+docs.rs page "memra-engine 0.125.0 src/bin/glm5_prime_v2_gate.rs").  Every
+output must be finite.
 """
 import numpy as np
 

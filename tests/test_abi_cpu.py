@@ -13,7 +13,7 @@ import mhc_hyper_connection_token_amd as mhc
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mhc.h")
 
-OK, EINVAL, EALIGN, EUNSUP, EHIP, EOVERLAP = range(6)
+OK, EINVAL, EALIGN, EUNSUP, EHIP, EOVERLAP, ECAPTURE = range(7)
 
 
 @pytest.fixture(scope="module")
@@ -45,8 +45,9 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for rc in range(6):
+    for rc in range(7):
         assert lib.mhc_status_string(rc)
+    assert b"captured" in lib.mhc_status_string(ECAPTURE)
     assert lib.mhc_status_string(99) == b"unknown status"
 
 
@@ -306,3 +307,22 @@ def test_packed_weight_calls_refuse_before_any_gpu_work(lib):
                                    o1, o2, o3, o4, None) == EOVERLAP
     assert lib.mhc_site_pre_packed(x, w, vp(base_addr + 4 * step + 4), sc, bs, 300, 4, 4096, 20,
                                    ctypes.c_float(1e-6), o1, o2, o3, o4, None) == EALIGN
+
+
+def test_pre_scratch_bytes_follow_the_kernel_choice(lib):
+    """The library scratch a pre call needs: a 256-byte header plus the packed
+    weight where the token-tiled kernel runs (S <= 4, T >= 256), else the split
+    reduction's partials, G K-ranges x T tokens x (R + 1) floats."""
+    hdr = 256
+    packed = mhc.packed_weight_bytes(4, 4096)
+    assert packed == 8 * 4 * 8 * 6 * 64 * 16  # 8 waves x 32 chunks x 6 row groups x 1 KiB
+    assert mhc.site_pre_scratch_bytes(4096, 4, 4096) == hdr + packed
+    assert mhc.site_pre_scratch_bytes(256, 4, 4096) == hdr + packed
+    # below 256 tokens: the solo K-split, 128 ranges of 8 chunks of 16 floats
+    for T in (1, 4, 8, 255):
+        assert mhc.site_pre_scratch_bytes(T, 4, 4096) == hdr + 128 * T * 25 * 4
+    # the wide site: 64-token tiles, 16 tiles -> 32 K-ranges
+    assert mhc.site_pre_scratch_bytes(1024, 8, 7168) == hdr + 32 * 1024 * 81 * 4
+    # rejected shapes need nothing
+    for T, S, H in ((0, 4, 4096), (-1, 4, 4096), (4, 9, 4096), (4, 4, 6), (4, 0, 64)):
+        assert mhc.site_pre_scratch_bytes(T, S, H) == 0

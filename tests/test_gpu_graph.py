@@ -72,3 +72,65 @@ def test_graph_replays_match_eager(mhc, T, S, H):
         got = list(out_pre) + [out_x]
         for name, a, b in zip(("pre", "post", "comb", "y", "x_out"), got, ref):
             assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager result"
+
+
+def test_graph_survives_scratch_growth_and_capture_refuses_growth(mhc):
+    """A graph captured while the library scratch was small stays valid after an
+    eager call grows the scratch (the old area is never freed), and a call that
+    would have to grow the scratch while its stream is being captured is refused
+    with MHC_ECAPTURE before anything is enqueued."""
+    iters, eps = 20, 1e-6
+    T, S, H = 1, 4, 4096
+    print("[case] graph across scratch growth", flush=True)
+    d = {k: torch.from_numpy(v).cuda() for k, v in make_random_shape(T, S, H, 11).items()}
+    out_pre, out_x = _alloc(T, S, H)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        _site(mhc, d, iters, eps, out_pre, out_x)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in out_pre] + [out_x.clone()]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        _site(mhc, d, iters, eps, out_pre, out_x)
+    torch.cuda.synchronize()
+
+    # an eager call whose scratch exceeds anything this suite uses before it (the
+    # largest, the decode-exact prefill call, needs 52 MB): the decode-exact path
+    # at 4096 tokens, 8 streams, 64 K-ranges x 4096 tokens x 81 floats = 85 MB
+    TB, SB, HB = 4096, 8, 1024
+    need = 64 * TB * 81 * 4
+    assert need > 80 << 20
+    big = {k: torch.from_numpy(v).cuda() for k, v in make_random_shape(TB, SB, HB, 12).items()}
+    bpre, _ = _alloc(TB, SB, HB)
+    mhc.site_pre(big["x"], big["fn_w"], big["scale"], big["base"], iters, eps, out=bpre,
+                 exact=True)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in list(out_pre) + [out_x]:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = list(out_pre) + [out_x]
+        for name, a, b in zip(("pre", "post", "comb", "y", "x_out"), got, ref):
+            assert torch.equal(a, b), f"replay {rep} after growth: {name} differs"
+
+    # growth under capture: refused, nothing enqueued
+    TC = 8192  # twice the tokens: more scratch than the current area holds
+    assert 64 * TC * 81 * 4 > need + need // 4 + 256
+    xc = torch.zeros((TC, SB, HB), device="cuda")
+    cpre, _ = _alloc(TC, SB, HB)
+    g2 = torch.cuda.CUDAGraph()
+    with pytest.raises(mhc.MhcError) as ei:
+        with torch.cuda.graph(g2, stream=s):
+            mhc.site_pre(xc, big["fn_w"], big["scale"], big["base"], iters, eps, out=cpre,
+                         exact=True)
+    assert ei.value.status == 6  # MHC_ECAPTURE
+    torch.cuda.synchronize()
+    # the library still works eagerly afterwards
+    with torch.cuda.stream(s):
+        _site(mhc, d, iters, eps, out_pre, out_x)
+    torch.cuda.synchronize()
+    for a, b in zip(list(out_pre) + [out_x], ref):
+        assert torch.equal(a, b)
