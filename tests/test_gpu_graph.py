@@ -1,7 +1,8 @@
 """HIP graph capture of whole sites: every replay equals the eager result bit for bit.
 
 Covers the three pre schedules (single-launch decode, split partials + finish,
-packed-weight fused tiles) and the post kernel.  Between replays the program
+packed-weight fused tiles) and the post kernel.  Every replay is also compared
+with the fp64 oracle on every token.  Between replays the program
 runs its own eager work (a different site through the same library scratch)
 and synchronises, so a replay that depended on state left by the capture, or
 on memory cleared only once, would differ.
@@ -9,7 +10,9 @@ on memory cleared only once, would differ.
 import numpy as np
 import pytest
 
+import oracle
 from mhc_inputs import make_random_shape
+from parity import check_site_with_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -61,6 +64,9 @@ def test_graph_replays_match_eager(mhc, T, S, H):
         _site(mhc, d, iters, eps, out_pre, out_x)
     torch.cuda.synchronize()
 
+    host = {k: v.cpu().numpy() for k, v in d.items()}
+    o_ref = oracle.site_pre(host["x"], host["fn_w"], host["scale"], host["base"], iters,
+                            float(np.float32(eps)))
     for rep in range(3):
         for t in list(out_pre) + [out_x]:
             t.fill_(float("nan"))
@@ -72,6 +78,10 @@ def test_graph_replays_match_eager(mhc, T, S, H):
         got = list(out_pre) + [out_x]
         for name, a, b in zip(("pre", "post", "comb", "y", "x_out"), got, ref):
             assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager result"
+        # the replay's outputs against the fp64 oracle, every token
+        check_site_with_oracle(host["x"], host, [t.cpu().numpy() for t in out_pre], iters, eps,
+                               f"graph T{T} S{S} H{H} replay {rep}",
+                               x_out=out_x.cpu().numpy(), oracle_pre=o_ref)
 
 
 def test_graph_survives_scratch_growth_and_capture_refuses_growth(mhc):

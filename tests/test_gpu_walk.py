@@ -1,13 +1,13 @@
 """A walk over sites with mhc_site_post_pre (the post half of a site fused with
 the pre half of the next) must be bit-identical to the same walk with separate
-mhc_site_pre / mhc_site_post calls, and every site within the oracle's
-tolerances, with and without the branch-input epilogue."""
+mhc_site_pre / mhc_site_post calls, and every site (every token, pre outputs and
+post mix) within the oracle's tolerances, with and without the branch-input
+epilogue."""
 import numpy as np
 import pytest
 
-import oracle
 from mhc_inputs import make_norm_weight, make_random_shape
-from parity import assert_gates_close, assert_streams_close
+from parity import check_site_with_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -92,12 +92,9 @@ def test_fused_walk_equals_separate_calls(mhc, T, S, H, zq):
         assert torch.equal(x1, x2), f"site {k}: input state differs"
         for u, v in zip(o1, o2):
             assert torch.equal(u, v), f"site {k}: outputs differ"
-    # every site of the walk against the oracle, on sampled tokens
-    rows = np.unique([0, T // 2, T - 1])
-    for k, (xs, o) in enumerate(ob):
-        xh = xs.cpu().numpy()[rows]
-        s = sites[k]
-        ref = oracle.site_pre(xh, s["fn_w"], s["scale"], s["base"], ITERS, float(np.float32(EPS)))
-        assert_gates_close(o[1].cpu().numpy()[rows], ref["post"], f"site {k} post")
-        assert_gates_close(o[2].cpu().numpy()[rows], ref["comb"], f"site {k} comb")
-        assert_streams_close(o[3].cpu().numpy()[rows], ref["y"], f"site {k} y")
+    # every site of the walk against the oracle, every token: its pre outputs
+    # from its input state, and its post mix into the next site's input state
+    nxt = [xs for xs, _ in ob[1:]] + [xb]
+    for k, ((xs, o), xn) in enumerate(zip(ob, nxt)):
+        check_site_with_oracle(xs.cpu().numpy(), sites[k], [v.cpu().numpy() for v in o[:4]],
+                               ITERS, EPS, f"walk site {k}", x_out=xn.cpu().numpy())

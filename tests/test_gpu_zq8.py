@@ -4,7 +4,9 @@ with a norm weight and its q8 codes, against the fp64 oracle.
 z is compared with the oracle's norm of the GPU's own y (isolating the
 epilogue) and with the oracle's norm of the oracle's y (end to end).  The int8
 codes and block scales are decided in fp32, so they must equal, bit for bit,
-the oracle's fp32 quantiser applied to the z the GPU wrote."""
+the oracle's fp32 quantiser applied to the z the GPU wrote; against the
+oracle's quantiser on the oracle's own z they agree within the stream
+tolerance (scales) and one step (codes)."""
 import numpy as np
 import pytest
 
@@ -56,6 +58,15 @@ def _check(mhc, d, iters, eps, label, tokens=None):
     assert np.array_equal(dd[idx], do), f"{label}: block scales differ"
     assert np.array_equal(q[idx], qo), f"{label}: q8 codes differ"
     assert np.all(np.abs(q.astype(np.int32)) <= 127)
+    # end to end: the oracle's quantiser on the oracle's own z (rounded to fp32,
+    # the precision the codes are decided in).  z differs by at most the stream
+    # tolerance, so each scale is within it (relative to the token's largest
+    # scale) and a code moves by at most one step where z sits near a rounding
+    # boundary.
+    qe, de = oracle.q8(zo.astype(np.float32))
+    assert_streams_close(dd[idx], de, f"{label} block scales (end to end)")
+    dq = np.abs(q[idx].astype(np.int32) - qe.astype(np.int32))
+    assert dq.max(initial=0) <= 1, f"{label}: a code differs by {dq.max()} end to end"
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode", "verify4", "verify8"])
@@ -64,10 +75,9 @@ def test_zq8_configs(mhc, name):
     _check(mhc, make_site(c), c.iters, c.eps, name)
 
 
-def test_zq8_prefill_sampled(mhc):
+def test_zq8_prefill_every_token(mhc):
     c = CONFIGS["prefill"]
-    toks = [0, 1, 2, 3, 127, 128, 2048, 4093, 4094, 4095]
-    _check(mhc, make_site(c), c.iters, c.eps, "prefill", tokens=toks)
+    _check(mhc, make_site(c), c.iters, c.eps, "prefill")
 
 
 # Paths: one token with S <= 4 runs the epilogue in the single-launch decode
