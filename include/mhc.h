@@ -108,6 +108,24 @@ int mhc_site_pre(const float* x, const float* fn_w, const float* scale, const fl
 size_t mhc_site_pre_scratch_bytes(int T, int streams, int hidden);
 
 /*
+ * mhc_site_pre_static -- mhc_site_pre for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, checks, kernels and results, but the kernel
+ * scratch is a fixed device array inside the library, 16 MiB on each GPU the
+ * process uses, held until the process ends.  The call allocates, frees and
+ * clears nothing.  A shape whose scratch (mhc_site_pre_scratch_bytes minus its
+ * 256-byte header) exceeds 16 MiB returns MHC_EUNSUPPORTED before anything is
+ * enqueued (large batches of short slabs can need more; the decode, verify,
+ * prefill and wide sites need at most 10.7 MB).  Every call on a GPU shares that GPU's array
+ * (the last call's contents stay in it): two calls that overlap in time on one
+ * GPU (different streams, or concurrent graph replays) race on it and must be
+ * ordered by the caller.
+ */
+int mhc_site_pre_static(const float* x, const float* fn_w, const float* scale, const float* base,
+                        int T, int streams, int hidden, int iters, float eps, float* pre,
+                        float* post, float* comb, float* y, void* stream);
+
+/*
  * mhc_site_post -- the post half of one site (hyper.rs, doc comment of `post`):
  *   x_out[t,k,i] = post[t,k] * f[t,i] + sum_j comb[t,j,k] * x[t,j,i]
  * where x is the SITE's input state (the same x given to mhc_site_pre) and f the

@@ -36,7 +36,8 @@ EXPORTED_SYMBOLS = ("mhc_site_pre", "mhc_site_post", "mhc_site_pre_exact", "mhc_
                     "mhc_site_post_pre", "mhc_site_post_pre_zq8", "mhc_site_post_pre_check",
                     "mhc_status_string", "mhc_probe_sink_floats", "mhc_bandwidth_probe",
                     "mhc_packed_weight_bytes", "mhc_pack_weight", "mhc_site_pre_packed",
-                    "mhc_site_post_pre_packed", "mhc_site_pre_scratch_bytes")
+                    "mhc_site_post_pre_packed", "mhc_site_pre_scratch_bytes",
+                    "mhc_site_pre_static")
 
 STATUS = {0: "MHC_OK", 1: "MHC_EINVAL", 2: "MHC_EALIGN", 3: "MHC_EUNSUPPORTED",
           4: "MHC_EHIP", 5: "MHC_EOVERLAP", 6: "MHC_ECAPTURE"}
@@ -117,6 +118,8 @@ def load_library() -> ctypes.CDLL:
     lib.mhc_site_post_pre_packed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, fl, vp,
                                              vp, vp, vp, vp, vp]
     lib.mhc_site_post_pre_packed.restype = i
+    lib.mhc_site_pre_static.argtypes = [vp, vp, vp, vp, i, i, i, i, fl, vp, vp, vp, vp, vp]
+    lib.mhc_site_pre_static.restype = i
     lib.mhc_site_pre_scratch_bytes.argtypes = [i, i, i]
     lib.mhc_site_pre_scratch_bytes.restype = sz
     lib.mhc_probe_sink_floats.argtypes = [sz]
@@ -162,13 +165,15 @@ def _stream_handle(stream):
 
 
 def site_pre(x, fn_w, scale, base, iters: int, eps: float, *, out=None, stream=None,
-             exact: bool = False, packed=None):
+             exact: bool = False, packed=None, static_scratch: bool = False):
     """Pre half of a site.  x: [T,S,H]; fn_w: [(2+S)*S, S*H]; scale: [3]; base: [(2+S)*S].
     Returns (pre [T,S], post [T,S], comb [T,S,S], y [T,H]); `out` may supply that tuple.
     exact=True calls mhc_site_pre_exact (every row bit-identical to a solo T=1 call);
-    packed (from pack_weight) calls mhc_site_pre_packed (same results, no per-call pack)."""
-    if exact and packed is not None:
-        raise ValueError("exact and packed are separate calls")
+    packed (from pack_weight) calls mhc_site_pre_packed (same results, no per-call pack);
+    static_scratch=True calls mhc_site_pre_static (the library's fixed scratch array,
+    no device allocation by the library; pass `out` to allocate nothing at all)."""
+    if (exact, packed is not None, static_scratch).count(True) > 1:
+        raise ValueError("exact, packed and static_scratch are separate calls")
     import torch
     lib = load_library()
     if x.dim() != 3:
@@ -195,8 +200,12 @@ def site_pre(x, fn_w, scale, base, iters: int, eps: float, *, out=None, stream=N
         if rc != 0:
             raise MhcError("mhc_site_pre_packed", rc, _status_text(lib, rc))
         return out
-    fn, name = ((lib.mhc_site_pre_exact, "mhc_site_pre_exact") if exact
-                else (lib.mhc_site_pre, "mhc_site_pre"))
+    if exact:
+        fn, name = lib.mhc_site_pre_exact, "mhc_site_pre_exact"
+    elif static_scratch:
+        fn, name = lib.mhc_site_pre_static, "mhc_site_pre_static"
+    else:
+        fn, name = lib.mhc_site_pre, "mhc_site_pre"
     rc = fn(px, pw, ps, pb, T, S, H, int(iters), float(eps), *ptrs, _stream_handle(stream))
     if rc != 0:
         raise MhcError(name, rc, _status_text(lib, rc))

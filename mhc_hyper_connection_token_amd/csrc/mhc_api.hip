@@ -272,7 +272,7 @@ int site_pre_run(const float* x, const float* fn_w, const float* scale, const fl
     if ((rc = acquire_scratch(src, p.part_floats * sizeof(float), st, &sc))) return rc;
     float* part = sc.general;
     hipError_t e;
-    if (zq && mhc::decode_zq8_supported(T, S, H, p.G)) {
+    if (zq && sc.counter && mhc::decode_zq8_supported(T, S, H, p.G)) {
       // one decode token with the epilogue: one launch; the block that draws
       // the last ticket finishes
       e = mhc::launch_decode_zq8(x, fn_w, scale, base, T, S, H, iters, eps, p.G, p.cpr, part,
@@ -818,6 +818,64 @@ int mhc_ws_site_post(mhc_workspace* ws, const float* f, int T, void* stream) {
     return MHC_EHIP;
   ws->cur ^= 1;
   return MHC_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- no-allocation pre call
+// mhc_site_pre_static: mhc_site_pre with its kernel scratch (the packed weight
+// of the token-tiled kernel, or the split reduction's partial sums) in a
+// fixed device array of this library instead of the growable library scratch,
+// so that the call never allocates, frees or clears device memory.  Every
+// process that loads the library holds kStaticScratchBytes of it on each GPU
+// it runs on, until the process ends.  The array's host-side name is not a
+// device address: its address on each device comes from hipGetSymbolAddress,
+// taken once per device (with that device current) and kept.  Nothing in the
+// array has to start at zero: the pre chain writes every scratch value before
+// reading it.
+namespace {
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_static_mu;
+void* g_static_ptr[64];
+
+int static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MHC_EHIP;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MHC_EHIP;
+    g_static_ptr[dev] = p;
+  }
+  *out = g_static_ptr[dev];
+  return MHC_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int mhc_site_pre_static(const float* x, const float* fn_w, const float* scale, const float* base,
+                        int T, int streams, int hidden, int iters, float eps, float* pre,
+                        float* post, float* comb, float* y, void* stream) {
+  int rc = mhc_site_pre_check(x, fn_w, scale, base, T, streams, hidden, iters, eps, pre, post,
+                              comb, y);
+  if (rc || T == 0) return rc;
+  const size_t need = pre_scratch_bytes(T, streams, hidden);
+  if (need > kStaticScratchBytes) return MHC_EUNSUPPORTED;
+  void* p = nullptr;
+  if ((rc = static_scratch(&p))) return rc;
+  // the pre chain without the epilogue uses no ticket, so the whole array is
+  // the general region
+  Scratch holder;
+  holder.general = static_cast<float*>(p);
+  holder.counter = nullptr;
+  ScratchSource src;
+  src.fixed = &holder;
+  src.bytes = kStaticScratchBytes;
+  return site_pre_run(x, fn_w, scale, base, T, streams, hidden, iters, eps, pre, post, comb, y,
+                      nullptr, static_cast<hipStream_t>(stream), src);
 }
 
 }  // extern "C"
