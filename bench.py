@@ -43,8 +43,11 @@ def kernel_source_hash(names):
 # kernel -> the source files whose change invalidates its measured traffic
 KERNEL_SOURCES = {
     "post_kernel": ["mhc_post.hip", "mhc_device.h"],
+    "pre_kernel": ["mhc_fused.hip", "mhc_device.h"],
     "pre_call": ["mhc_fused.hip", "mhc_device.h"],
     "walk_call": ["mhc_fused.hip", "mhc_device.h"],
+    "wide_pre_call": ["mhc_partials.hip", "mhc_split.h", "mhc_finish.hip", "mhc_device.h"],
+    "wide_post_kernel": ["mhc_post.hip", "mhc_device.h"],
 }
 
 
@@ -139,6 +142,21 @@ def time_site(mhc, torch, t, c, out_pre, out_x, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return start.elapsed_time(end) / steps, pre_ms, post_ms, wall, eager_ms
+
+
+def time_kernels_alone(mhc, torch, t, c, out_pre, out_x, calls=20, reps=5):
+    """Device µs per launch of the token-tiled pre kernel alone (the packed-weight
+    pre call, whose only launch it is at this size) and of the post kernel, each
+    from time_graph (HIP graph of `calls` launches, events on its stream)."""
+    packed = mhc.pack_weight(t["fn_w"], c.S, c.H)
+    torch.cuda.synchronize()
+    pre_us = time_graph(torch, lambda: mhc.site_pre(
+        t["x"], t["fn_w"], t["scale"], t["base"], c.iters, c.eps, out=out_pre, packed=packed),
+        calls=calls, reps=reps)
+    post_us = time_graph(torch, lambda: mhc.site_post(
+        t["x"], t["f"], out_pre[1], out_pre[2], out=out_x), calls=calls, reps=reps)
+    del packed
+    return {"pre_kernel_us": pre_us, "post_kernel_us": post_us}
 
 
 def time_site_packed(mhc, torch, t, c, out_pre, out_x, steps):
@@ -548,6 +566,51 @@ def cpu_baseline(c, d, cpu_seconds=15.0, max_wall=30.0):
                       f"workload, pre + post, {dt:.2f} s wall on {threads} threads"}
 
 
+def oracle_per_config(cpu_seconds_cap=8.0):
+    """The fp64 oracle (pre + post) on every workload config, at all host cores
+    and at one thread, median of 3 runs each.  A config whose full run would
+    take more than `cpu_seconds_cap` seconds of one core is timed on a prefix of
+    its tokens (the oracle is per token, so its rate does not depend on T), and
+    the token count is reported."""
+    import statistics
+
+    import numpy as np
+
+    import oracle
+    from mhc_inputs import CONFIGS, make_site
+    cores = oracle.default_threads()
+    rows = {}
+    for name in ("tiny", "decode", "verify4", "verify8", "prefill", "wide"):
+        c = CONFIGS[name]
+        d = make_site(c)
+        eps = float(np.float32(c.eps))
+
+        def run(n, threads):
+            t0 = time.perf_counter()
+            o = oracle.site_pre(d["x"][:n], d["fn_w"], d["scale"], d["base"], c.iters, eps,
+                                nthreads=threads)
+            oracle.site_post(d["x"][:n], d["f"][:n], o["post"].astype(np.float32),
+                             o["comb"].astype(np.float32), nthreads=threads)
+            return time.perf_counter() - t0
+
+        probe_n = min(c.T, 16)
+        per_tok_1 = run(probe_n, 1) / probe_n
+        n1 = int(min(c.T, max(1, cpu_seconds_cap / max(per_tok_1, 1e-9))))
+        one = statistics.median(run(n1, 1) for _ in range(3))
+        alln = statistics.median(run(c.T, cores) for _ in range(3))
+        rows[name] = {"T": c.T, "streams": c.S, "hidden": c.H,
+                      "all_cores_ms": round(alln * 1e3, 3),
+                      "all_cores_tokens_per_s": round(c.T / alln, 1),
+                      "one_thread_tokens": n1,
+                      "one_thread_ms": round(one * 1e3, 3),
+                      "one_thread_tokens_per_s": round(n1 / one, 1)}
+    return {"cores": cores, "configs": rows,
+            "note": "fp64 oracle, pre + post (post fed the oracle's own gates rounded to "
+                    "fp32), wall clock, median of 3; all_cores: every token of the config "
+                    "on all host threads; one_thread: one thread on the first "
+                    "one_thread_tokens tokens"}
+
+
 def load_traffic(kernel):
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -562,9 +625,12 @@ def load_traffic(kernel):
 
 # prefill kernels whose counters make up each measured unit
 TRAFFIC_UNITS = {
+    "pre_kernel": ["fused_pre_kernel<4, 8, 1, false, false, false>"],
     "pre_call": ["pack_weight_kernel<4, 24, 8>", "fused_pre_kernel<4, 8, 1, false, false, false>"],
     "post_kernel": ["post_kernel<4>"],
     "walk_call": ["pack_weight_kernel<4, 24, 8>", "fused_pre_kernel<4, 8, 1, false, true, false>"],
+    "wide_pre_call": ["partials_kernel<5, 4>", "finish_kernel<8>"],
+    "wide_post_kernel": ["post_kernel<8>"],
 }
 
 
@@ -677,16 +743,34 @@ def main():
     packed_ms = time_site_packed(mhc, torch, t, c, out_pre, out_x, args.steps)
     pre_b, post_b = algorithmic_bytes(c.T, c.S, c.H)
     site_gbps = (pre_b + post_b) / (ms * 1e-3) / 1e9
-    if post_ms >= pre_ms:
-        dom, dom_ms, dom_b, bound_name = "post_kernel", post_ms, post_b, "mhc_site_post (post_kernel)"
+    # The dominant kernel: the token-tiled pre kernel alone (mhc_site_pre_packed
+    # with the weight packed beforehand launches only it) against the post
+    # kernel, each as K launches captured in a HIP graph and replayed, HIP
+    # events on the stream the kernels run on.  The pre kernel moves the pre
+    # call's algorithmic bytes (x, the weight once, y and the gates).
+    kern = time_kernels_alone(mhc, torch, t, c, out_pre, out_x, calls=max(10, args.steps // 2))
+    if kern["post_kernel_us"] >= kern["pre_kernel_us"]:
+        dom, dom_us, dom_b, bound_name = ("post_kernel", kern["post_kernel_us"], post_b,
+                                          "post_kernel<4> (mhc_site_post)")
     else:
-        dom, dom_ms, dom_b, bound_name = ("pre_call", pre_ms, pre_b,
-                                          "mhc_site_pre (pack_weight_kernel + fused_pre_kernel)")
-    achieved = dom_b / (dom_ms * 1e-3) / 1e9
+        dom, dom_us, dom_b, bound_name = (
+            "pre_kernel", kern["pre_kernel_us"], pre_b,
+            "fused_pre_kernel<4,8,1,false,false,false> (mhc_site_pre's token-tiled pre chain; "
+            "the weight pack is a kernel of its own)")
+    achieved = dom_b / (dom_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": bound_name, "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
                 "traffic": load_traffic(dom), "algorithmic_bytes_per_launch": dom_b,
-                "avg_launch_us": round(dom_ms * 1e3, 2)}
+                "avg_launch_us": round(dom_us, 2),
+                "other_kernel_us": round(kern["post_kernel_us"] if dom == "pre_kernel"
+                                         else kern["pre_kernel_us"], 2),
+                "pre_call_eager_us": round(pre_ms * 1e3, 2),
+                "note": "avg_launch_us: the kernel alone, K launches in one HIP graph replayed, "
+                        "HIP events on its stream; achieved = algorithmic bytes per launch / "
+                        "avg_launch_us; traffic = 2.0 x FETCH_SIZE + WRITE_SIZE of one launch "
+                        "(rocprofv3 counters scaled by a plain copy), null if the kernel's "
+                        "sources changed since; pre_call_eager_us: pack + pre kernel as one "
+                        "eager call"}
 
     # ---- decode site (T=1): microseconds per site, back to back
     cd = CONFIGS["decode"]
@@ -851,8 +935,11 @@ def main():
     ex = {k: round(v, 2) for k, v in ex.items()}
     del d64, p64
 
-    # ---- CPU oracle baseline (host cores, bounded sample)
+    # ---- CPU oracle baseline (host cores, bounded sample), and the oracle on
+    # every config at all cores and at one thread
     cpu = None if args.no_cpu_baseline else cpu_baseline(c, d)
+    if cpu is not None:
+        cpu["per_config"] = oracle_per_config()
 
     line = {
         "metric": METRIC,

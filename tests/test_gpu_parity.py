@@ -99,8 +99,14 @@ def test_config_parity_full_size_every_token(mhc, name):
     (257, 4, 68, 20), (320, 1, 8192, 20),
     # S > 4 from 512 tokens: 64-token MFMA blocks with a partly empty last block
     (513, 8, 1024, 20), (700, 6, 516, 20), (1000, 5, 260, 3), (577, 7, 128, 20),
-    # the fused tiles at S = 4 with a ragged last tile
-    (1025, 4, 1024, 20), (2047, 4, 2048, 1),
+    # the fused tiles at S = 4 with a ragged last tile, and large batches of
+    # every stream count (a tile count the grid does not divide, 200 Sinkhorn
+    # rounds, the largest token count of the ragged set)
+    (1025, 4, 1024, 20), (2047, 4, 2048, 1), (512, 4, 4096, 20), (513, 3, 1536, 20),
+    (1040, 2, 512, 20), (4097, 4, 4096, 20), (5000, 1, 3072, 7), (700, 4, 2048, 200),
+    (2100, 3, 4096, 20), (8192, 2, 1024, 20),
+    # large batches whose slab does not fit the fused tiles (split path)
+    (600, 4, 4100, 20), (1030, 2, 2560, 20),
 ])
 def test_ragged_shapes(mhc, T, S, H, iters):
     _say(f"ragged T={T} S={S} H={H} iters={iters}")
@@ -229,3 +235,15 @@ def test_red_arm_one_iteration_off_is_detected(mhc):
 def test_native_library_is_loaded(mhc):
     maps = open("/proc/self/maps").read()
     assert mhc.LIB_PATH in maps
+
+
+def test_large_batch_shapes_alternate(mhc):
+    """Large batches of different shapes (1 to 4 streams, fused tiles and the
+    split path) share the library scratch; calls that alternate between them
+    must each match the oracle on every token."""
+    seq = [(700, 4, 4096), (513, 3, 1536), (600, 2, 2048), (1040, 1, 512), (700, 4, 4096),
+           (513, 3, 1536), (530, 4, 512), (600, 2, 2048)]
+    for i, (T, S, H) in enumerate(seq):
+        _say(f"alternating group shapes: call {i} T={T} S={S} H={H}")
+        d = make_random_shape(T, S, H, seed=400 + i)
+        _check_site(mhc, d, 20, 1e-6, label=f"call{i} T{T}S{S}H{H}")
