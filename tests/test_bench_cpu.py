@@ -53,14 +53,20 @@ def test_write_traffic_scales_by_the_copy_kernel(tmp_path, monkeypatch):
         ("void mhc::fused_pre_kernel<4, 8, 1, false, false, false>(...)", 524288, 100000.0),
         ("void mhc::fused_pre_kernel<4, 8, 1, false, false, false>(...)", 1024, 5.0),  # decode-size
         ("void mhc::post_kernel<4>(...)", 4194304, 160000.0),
-        ("void mhc::fused_pre_kernel<4, 8, 1, false, true, false>(...)", 524288, 150000.0)])
+        ("void mhc::fused_pre_kernel<4, 8, 1, false, true, false>(...)", 524288, 150000.0),
+        ("void mhc::partials_kernel<5, 4>(...)", 131072, 210000.0),
+        ("void mhc::finish_kernel<8>(...)", 262144, 120000.0),
+        ("void mhc::post_kernel<8>(...)", 1835008, 130000.0)])
     _counter_db(write, "WRITE_SIZE", [
         (copy, 1 << 20, 262144.0),
         ("void mhc::pack_weight_kernel<4, 24, 8>(float const*)", 98304, 1536.0),
         ("void mhc::fused_pre_kernel<4, 8, 1, false, false, false>(...)", 524288, 60000.0),
         ("void mhc::fused_pre_kernel<4, 8, 1, false, false, false>(...)", 1024, 1.0),
         ("void mhc::post_kernel<4>(...)", 4194304, 262144.0),
-        ("void mhc::fused_pre_kernel<4, 8, 1, false, true, false>(...)", 524288, 330000.0)])
+        ("void mhc::fused_pre_kernel<4, 8, 1, false, true, false>(...)", 524288, 330000.0),
+        ("void mhc::partials_kernel<5, 4>(...)", 131072, 12000.0),
+        ("void mhc::finish_kernel<8>(...)", 262144, 29000.0),
+        ("void mhc::post_kernel<8>(...)", 1835008, 229376.0)])
     out = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
     bench.write_traffic(fetch, write)
@@ -72,6 +78,11 @@ def test_write_traffic_scales_by_the_copy_kernel(tmp_path, monkeypatch):
     # the walk kernel is told apart from the plain one by its template arguments
     assert rec["walk_call"]["bytes_per_launch"] == round((2 * 800 + 1536 + 2 * 150000 + 330000)
                                                          * 1024)
+    # the fused kernel alone, and the wide site's calls (S = 8 has kernels of its own)
+    assert rec["pre_kernel"]["bytes_per_launch"] == round((2 * 100000 + 60000) * 1024)
+    assert rec["wide_pre_call"]["bytes_per_launch"] == round((2 * 210000 + 12000 + 2 * 120000
+                                                              + 29000) * 1024)
+    assert rec["wide_post_kernel"]["bytes_per_launch"] == round((2 * 130000 + 229376) * 1024)
     # the stored hash is that of the measured kernels' sources
     assert rec["pre_call"]["source_hash"] == bench.kernel_source_hash(bench.KERNEL_SOURCES["pre_call"])
 
