@@ -8,8 +8,8 @@ import pytest
 
 import oracle
 from mhc_inputs import CONFIGS, make_random_shape, make_site
-from parity import (assert_gates_close, assert_streams_close, gate_violation, relative,
-                    STREAM_REL)
+from parity import (assert_gates_close, assert_streams_close, check_site_with_oracle,
+                    gate_violation, relative, STREAM_REL)
 
 pytestmark = pytest.mark.gpu
 
@@ -247,3 +247,39 @@ def test_large_batch_shapes_alternate(mhc):
         _say(f"alternating group shapes: call {i} T={T} S={S} H={H}")
         d = make_random_shape(T, S, H, seed=400 + i)
         _check_site(mhc, d, 20, 1e-6, label=f"call{i} T{T}S{S}H{H}")
+
+
+# ------------------------------------------------------------------ the largest batch accepted
+@pytest.mark.parametrize("S,H", [(4, 4096), (8, 7168)])
+def test_largest_accepted_batch(mhc, S, H):
+    """T*S*H one short of 2^31, the largest batch the calls accept (the fused
+    token tiles at S = 4, the split path at S = 8): byte offsets into x and x'
+    pass 2^31 and 2^32.  x and f are drawn on the device (U[-1, 1), like the
+    configs, from a seeded generator); the outputs of a sample of tokens (the
+    first and last, both sides of each byte-offset power of two, and random
+    ones) are compared with the oracle run on those tokens alone, which is
+    exact because a token's outputs depend only on its own slab."""
+    n = S * H
+    T = (2 ** 31 - 1) // n
+    _say(f"largest batch T={T} S={S} H={H}")
+    small = make_random_shape(1, S, H, seed=4242 + S)
+    g = torch.Generator(device="cuda").manual_seed(1000 + S)
+    x = torch.empty((T, S, H), device="cuda").uniform_(-1.0, 1.0, generator=g)
+    f = torch.empty((T, H), device="cuda").uniform_(-1.0, 1.0, generator=g)
+    fn_w, scale, base = _dev(small["fn_w"]), _dev(small["scale"]), _dev(small["base"])
+    pre, post, comb, y = mhc.site_pre(x, fn_w, scale, base, 20, 1e-6)
+    xo = mhc.site_post(x, f, post, comb)
+    torch.cuda.synchronize()
+    pick = {0, 1, T - 2, T - 1}
+    for k in (31, 32, 33):
+        t = (2 ** k + 4 * n - 1) // (4 * n)  # first token whose slab starts at or past 2^k bytes
+        pick.update(u for u in (t - 1, t) if 0 <= u < T)
+    pick.update(np.random.default_rng(7 + S).choice(T, 24, replace=False).tolist())
+    idx = torch.tensor(sorted(pick), device="cuda")
+    site = {"fn_w": small["fn_w"], "scale": small["scale"], "base": small["base"],
+            "f": f[idx].cpu().numpy()}
+    outs = [o[idx].cpu().numpy() for o in (pre, post, comb, y)]
+    xs, xos = x[idx].cpu().numpy(), xo[idx].cpu().numpy()
+    del x, f, pre, post, comb, y, xo
+    torch.cuda.empty_cache()
+    check_site_with_oracle(xs, site, outs, 20, 1e-6, f"largest T{T}S{S}H{H}", x_out=xos)
