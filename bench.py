@@ -145,18 +145,34 @@ def time_site(mhc, torch, t, c, out_pre, out_x, steps, warmup):
 
 
 def time_kernels_alone(mhc, torch, t, c, out_pre, out_x, calls=20, reps=5):
-    """Device µs per launch of the token-tiled pre kernel alone (the packed-weight
-    pre call, whose only launch it is at this size) and of the post kernel, each
-    from time_graph (HIP graph of `calls` launches, events on its stream)."""
+    """Device µs per launch of the token-tiled pre kernel and of the post kernel,
+    each from time_graph (HIP graph of `calls` launches, HIP events on its
+    stream).  The pre kernel is timed where a site step runs it, right after the
+    weight pack: a graph of (pack, packed-weight pre call) pairs less a graph of
+    the packs alone.  Back to back with itself it runs slower; that figure is
+    returned as well."""
     packed = mhc.pack_weight(t["fn_w"], c.S, c.H)
     torch.cuda.synchronize()
-    pre_us = time_graph(torch, lambda: mhc.site_pre(
-        t["x"], t["fn_w"], t["scale"], t["base"], c.iters, c.eps, out=out_pre, packed=packed),
-        calls=calls, reps=reps)
+
+    def pre_packed():
+        mhc.site_pre(t["x"], t["fn_w"], t["scale"], t["base"], c.iters, c.eps, out=out_pre,
+                     packed=packed)
+
+    def pack():
+        mhc.pack_weight(t["fn_w"], c.S, c.H, out=packed)
+
+    def pack_then_pre():
+        pack()
+        pre_packed()
+
+    back_to_back_us = time_graph(torch, pre_packed, calls=calls, reps=reps)
+    pack_us = time_graph(torch, pack, calls=calls, reps=reps)
+    pair_us = time_graph(torch, pack_then_pre, calls=calls, reps=reps)
     post_us = time_graph(torch, lambda: mhc.site_post(
         t["x"], t["f"], out_pre[1], out_pre[2], out=out_x), calls=calls, reps=reps)
     del packed
-    return {"pre_kernel_us": pre_us, "post_kernel_us": post_us}
+    return {"pre_kernel_us": pair_us - pack_us, "pre_kernel_back_to_back_us": back_to_back_us,
+            "pack_kernel_us": pack_us, "post_kernel_us": post_us}
 
 
 def time_site_packed(mhc, torch, t, c, out_pre, out_x, steps):
@@ -625,8 +641,8 @@ def load_traffic(kernel):
 
 # prefill kernels whose counters make up each measured unit
 TRAFFIC_UNITS = {
-    "pre_kernel": ["fused_pre_kernel<4, 8, 1, false, false, false>"],
-    "pre_call": ["pack_weight_kernel<4, 24, 8>", "fused_pre_kernel<4, 8, 1, false, false, false>"],
+    "pre_kernel": ["fused_pf_kernel<4, 8>"],
+    "pre_call": ["pack_weight_kernel<4, 24, 8>", "fused_pf_kernel<4, 8>"],
     "post_kernel": ["post_kernel<4>"],
     "walk_call": ["pack_weight_kernel<4, 24, 8>", "fused_pre_kernel<4, 8, 1, false, true, false>"],
     "wide_pre_call": ["partials_kernel<5, 4>", "finish_kernel<8>"],
@@ -743,9 +759,9 @@ def main():
     packed_ms = time_site_packed(mhc, torch, t, c, out_pre, out_x, args.steps)
     pre_b, post_b = algorithmic_bytes(c.T, c.S, c.H)
     site_gbps = (pre_b + post_b) / (ms * 1e-3) / 1e9
-    # The dominant kernel: the token-tiled pre kernel alone (mhc_site_pre_packed
-    # with the weight packed beforehand launches only it) against the post
-    # kernel, each as K launches captured in a HIP graph and replayed, HIP
+    # The dominant kernel: the token-tiled pre kernel (mhc_site_pre_packed with
+    # the weight packed beforehand launches only it, timed after the pack as in
+    # a site step) against the post kernel, from HIP graphs of K launches, HIP
     # events on the stream the kernels run on.  The pre kernel moves the pre
     # call's algorithmic bytes (x, the weight once, y and the gates).
     kern = time_kernels_alone(mhc, torch, t, c, out_pre, out_x, calls=max(10, args.steps // 2))
@@ -755,8 +771,8 @@ def main():
     else:
         dom, dom_us, dom_b, bound_name = (
             "pre_kernel", kern["pre_kernel_us"], pre_b,
-            "fused_pre_kernel<4,8,1,false,false,false> (mhc_site_pre's token-tiled pre chain; "
-            "the weight pack is a kernel of its own)")
+            "fused_pf_kernel<4,8> (mhc_site_pre's token-tiled pre chain on persistent tiles, "
+            "half of each next slab requested into LDS; the weight pack is a kernel of its own)")
     achieved = dom_b / (dom_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": bound_name, "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
@@ -765,9 +781,13 @@ def main():
                 "other_kernel_us": round(kern["post_kernel_us"] if dom == "pre_kernel"
                                          else kern["pre_kernel_us"], 2),
                 "pre_call_eager_us": round(pre_ms * 1e3, 2),
-                "note": "avg_launch_us: the kernel alone, K launches in one HIP graph replayed, "
-                        "HIP events on its stream; achieved = algorithmic bytes per launch / "
-                        "avg_launch_us; traffic = 2.0 x FETCH_SIZE + WRITE_SIZE of one launch "
+                "pre_kernel_back_to_back_us": round(kern["pre_kernel_back_to_back_us"], 2),
+                "pack_kernel_us": round(kern["pack_kernel_us"], 2),
+                "note": "avg_launch_us: the pre kernel as a site step runs it, right after the "
+                        "weight pack: a HIP graph of K (pack, pre kernel) pairs less a graph of K "
+                        "packs, HIP events on their stream (pre_kernel_back_to_back_us: K pre "
+                        "launches with nothing between them); achieved = algorithmic bytes per "
+                        "launch / avg_launch_us; traffic = 2.0 x FETCH_SIZE + WRITE_SIZE of one launch "
                         "(rocprofv3 counters scaled by a plain copy), null if the kernel's "
                         "sources changed since; pre_call_eager_us: pack + pre kernel as one "
                         "eager call"}

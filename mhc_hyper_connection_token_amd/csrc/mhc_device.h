@@ -173,7 +173,10 @@ __device__ __forceinline__ void stage_site_params(const float* __restrict__ scal
 
 // Gates of up to NT tokens (NT = 4 for L = 4, 1 for L = 8) in ONE wavefront;
 // all 64 lanes must call it together.  With PRE = false the pre gates are left
-// to the caller (pre_gate), and pre / pre_lds are not touched.
+// to the caller (pre_gate), and pre / pre_lds are not touched.  With POST_NT the
+// post gates are non-temporal stores: a kernel with requests into LDS in flight
+// uses it, because the compiler otherwise merges the post store with the
+// pre_lds store into one flat store, which would wait for those requests.
 //   mraw + u*ldm : the unscaled dots fn_w[r,:].x[t,:] (r < R) of token slot u,
 //                  followed at index R by the token's sum of squares.
 //   params       : scale[0..2] then base[0..R-1] (see stage_site_params).
@@ -183,7 +186,7 @@ __device__ __forceinline__ void stage_site_params(const float* __restrict__ scal
 //   pre_lds      : pre gates for the collapse, slot u at + u*8.
 // Per token: rinv = 1/sqrt(ss/n + eps); m = raw*rinv; z = fma(scale_g, m, base);
 // pre = sigmoid(z), post = 2 sigmoid(z), comb = Sinkhorn(exp(z)).
-template <int L, bool PRE = true>
+template <int L, bool PRE = true, bool POST_NT = false>
 __device__ __forceinline__ void gates_wave(const float* mraw, int ldm, int ntok, int S, int n,
                                            const float* params, int iters, float eps,
                                            bool write_out, float* __restrict__ pre,
@@ -208,7 +211,12 @@ __device__ __forceinline__ void gates_wave(const float* mraw, int ldm, int ntok,
       } else {
         const float rinv = rms_inverse(mr[R], n, eps);
         const float v = 2.0f * sigmoid_exact_ends(fmaf(s_post, mr[g] * rinv, base[g]));
-        if (write_out) post[u * S + g - S] = v;
+        if (write_out) {
+          if (POST_NT)
+            __builtin_nontemporal_store(v, post + u * S + g - S);
+          else
+            post[u * S + g - S] = v;
+        }
       }
     }
   }

@@ -27,6 +27,8 @@
 // input state, branch output and gates, computes the post mix in registers,
 // writes it out as the new state, and runs this site's pre chain on it, so the
 // new state is never read back from memory.
+#include <atomic>
+
 #include "mhc_device.h"
 #include "mhc_kernels.h"
 
@@ -323,6 +325,225 @@ __global__ __launch_bounds__(512) void fused_pre_kernel(
   }
 }
 
+// ---------------------------------------------------------------- persistent tiles
+// The same token-tiled pre chain (fused_pre_kernel without the epilogue, the
+// post half or the head) on a persistent grid, for batches of four tiles or
+// more per compute unit: block b takes tiles b, b + G, b + 2G, ..., and after
+// a tile's last MFMA it requests tokens 2 and 3 of its next tile into LDS, so
+// that half of the next slab streams in while this tile reduces its partial
+// sums, runs the gates and the Sinkhorn and collapses.  On the next tile
+// those lanes take their slab from LDS, and their global loads are buffer
+// loads out of range, which fetch nothing; tokens 0 and 1 come from HBM as
+// in the fused kernel.  Every value a tile computes with is the one the fused
+// kernel loads, and every operation the same, so the outputs are
+// bit-identical to it.
+//
+// The request cannot start earlier.  A wave's memory operations complete in
+// issue order, and the compiler turns the first wait that follows a request
+// into LDS into a wait for every outstanding load (vmcnt(0)), so a request
+// issued inside the weight stream would stall it until the request lands.
+//
+// LDS: wave w's request for chunks 2p and 2p + 1 is one 1 KiB record p (lane
+// 32 (ci & 1) + 16 (token - 2) + bq), NCH / 2 records per wave, 128 KiB per
+// block at NCH = 32.
+
+// A block barrier for LDS hand-offs alone: the wave's LDS operations complete
+// (lgkmcnt(0)), then s_barrier.  __syncthreads() would also wait for the
+// next tile's LDS requests (its fence counts them in vmcnt), which have to
+// stay in flight through the tile's epilogue.  The empty asm statements keep
+// the compiler from moving memory operations across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt(63) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int S, int CPW>
+__global__ __launch_bounds__(512) void fused_pf_kernel(
+    const float* __restrict__ x, const float4* __restrict__ wpack,
+    const float* __restrict__ scale, const float* __restrict__ base, int T, int H, int iters,
+    float eps, float* __restrict__ pre, float* __restrict__ post, float* __restrict__ comb,
+    float* __restrict__ y) {
+  constexpr int R = (2 + S) * S;
+  constexpr int RG = (R + 3) / 4;
+  constexpr int NW = 8;
+  constexpr int NOUT = 4 * (R + 1);
+  constexpr int NCH = S * CPW;
+  constexpr int WD = 1;
+  static_assert(NCH % 2 == 0 && NCH <= 32, "two chunks per request record, 16 KiB per wave");
+  __shared__ float4 nxt[NW][NCH * 32];
+  __shared__ float red[NW][NOUT];
+  __shared__ float mr[4][R + 1];
+  __shared__ float pre_lds[4 * 8];
+  __shared__ float params[3 + R];
+
+  stage_site_params(scale, base, R, params);
+  const int n = S * H;
+  const int ntiles = (T + 3) / 4;
+
+  bool have = false;  // tokens 2 and 3 of this tile are in LDS (the same in every lane)
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    // Every lane-dependent value is derived from an opaque copy of the thread
+    // index in each tile: the values are the same in every tile, and kept
+    // across the tile loop they would hold registers the slab needs.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & (kWave - 1);
+    const int wave = tid >> 6;
+    const int tq = lane >> 4, bq = lane & 15;
+    const int src_lane4 = 4 * (16 * (lane & 3) + (lane >> 2));
+    const int wo = wave * NCH * RG * 64 + lane;  // this lane's first packed-weight entry
+    float4* mine = &nxt[wave][0];
+    // this lane's record entry for chunk ci (lanes of tokens 0 and 1 read an
+    // entry of token 2, which they discard)
+    const int rec_lane = 16 * ((tq - 2) & 1) + bq;
+    const int hb = 64 * wave * CPW + 4 * bq, tb = tq * n;
+    const int t0 = tile * 4;
+    const int tok = t0 + tq;
+    const bool tok_ok = tok < T;
+    const int next = tile + gridDim.x;
+    const bool want = next < ntiles;  // the same in every lane
+
+    // ---- the tile's slab: buffer loads straight into xr (lanes whose slab is
+    // in LDS, and tokens past T, are out of range and fetch nothing); the
+    // record entries replace those lanes' values as each chunk is consumed
+    const bool use_lds = have && tq >= 2;
+    const int valid = min(4, T - t0);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(x + (size_t)t0 * n), (short)0, valid * n * 4, 0x00020000);
+    float4 xr[NCH];
+#pragma unroll
+    for (int ci = 0; ci < NCH; ++ci) {
+      const int c = ci / CPW, u = ci % CPW;
+      const int h = hb + 64 * u;
+      const int off = use_lds ? 0x7FFFFFF0 : 4 * (tb + c * H + (h < H ? h : 0));
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2);
+      xr[ci] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                           __uint_as_float(v[3]));
+    }
+
+    // ---- weight stream and MFMAs, as in fused_pre_kernel
+    floatx4 acc[RG];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) acc[rg] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float ss = 0.f;
+    float4 wb[WD + 1][RG];
+    auto load_w = [&](int ci, float4* dst) {
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) dst[rg] = wpack[wo + (ci * RG + rg) * 64];
+    };
+#pragma unroll
+    for (int ci = 0; ci < WD && ci < NCH; ++ci) load_w(ci, wb[ci]);
+    // The request from the previous tile (issued before this tile's own loads,
+    // so complete once they are) has landed before any record is read.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ci = 0; ci < NCH; ++ci) {
+      if (ci + WD < NCH) load_w(ci + WD, wb[(ci + WD) % (WD + 1)]);
+      __builtin_amdgcn_sched_barrier(0);
+      const float4 lv = mine[(ci >> 1) * 64 + 32 * (ci & 1) + rec_lane];
+      const float4 v = use_lds ? lv : xr[ci];
+      xr[ci] = v;
+      if (64 * (wave * CPW + ci % CPW) + 4 * bq < H) {
+        ss = fmaf(v.x, v.x, ss);
+        ss = fmaf(v.y, v.y, ss);
+        ss = fmaf(v.z, v.z, ss);
+        ss = fmaf(v.w, v.w, ss);
+      }
+      int sl = src_lane4;
+      asm volatile("" : "+v"(sl));
+      const float ax = __int_as_float(__builtin_amdgcn_ds_bpermute(sl, __float_as_int(v.x)));
+      const float ay = __int_as_float(__builtin_amdgcn_ds_bpermute(sl, __float_as_int(v.y)));
+      const float az = __int_as_float(__builtin_amdgcn_ds_bpermute(sl, __float_as_int(v.z)));
+      const float aw = __int_as_float(__builtin_amdgcn_ds_bpermute(sl, __float_as_int(v.w)));
+      const float4* w = wb[ci % (WD + 1)];
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg)
+        acc[rg] = __builtin_amdgcn_mfma_f32_4x4x1f32(ax, w[rg].x, acc[rg], 0, 0, 0);
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg)
+        acc[rg] = __builtin_amdgcn_mfma_f32_4x4x1f32(ay, w[rg].y, acc[rg], 0, 0, 0);
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg)
+        acc[rg] = __builtin_amdgcn_mfma_f32_4x4x1f32(az, w[rg].z, acc[rg], 0, 0, 0);
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg)
+        acc[rg] = __builtin_amdgcn_mfma_f32_4x4x1f32(aw, w[rg].w, acc[rg], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    {
+      // Tokens 2 and 3 of the next tile, behind the tile's last weight load,
+      // its last read of the records and its last MFMA.  Issued on every tile,
+      // so that no wait depends on a branch; past the last tile every lane
+      // re-reads one small region of token 0, which stays in cache.
+      const int pc = (lane >> 5) & 1;
+      const int ptok = min(next * 4 + 2 + ((lane >> 4) & 1), T - 1);
+      const float* pt = want ? x + (size_t)ptok * n : x;
+      const int on = want ? 1 : 0;
+#pragma unroll
+      for (int p = 0; p < NCH / 2; ++p) {
+        const int cj = 2 * p + pc;
+        const int c = cj / CPW, u = cj % CPW;
+        const int h = hb + 64 * u;
+        __builtin_amdgcn_global_load_lds(pt + on * (c * H + (h < H ? h : 0)) + (1 - on) * 4 * bq,
+                                         &mine[p * 64], 16, 0, 2);
+      }
+    }
+
+    // ---- fixed-order reduction, gates, Sinkhorn (as in fused_pre_kernel)
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float t = sum_mfma4_blocks(acc[rg][v]);
+        if (lane < 4 && 4 * rg + lane < R) red[wave][v * (R + 1) + 4 * rg + lane] = t;
+      }
+    {
+      const float t = sum_row16(ss);
+      if ((lane & 15) == 0) red[wave][tq * (R + 1) + R] = t;
+    }
+    lds_barrier();
+    if (threadIdx.x < NOUT) {
+      const int o = threadIdx.x;
+      float sum = red[0][o];
+#pragma unroll
+      for (int ww = 1; ww < NW; ++ww) sum += red[ww][o];
+      mr[o / (R + 1)][o % (R + 1)] = sum;
+    }
+    lds_barrier();
+    if (wave == 0) {
+      const int ntok = min(4, T - t0);
+      gates_wave<4, true, true>(&mr[0][0], R + 1, ntok, S, n, params, iters, eps, true,
+                    pre + (size_t)t0 * S, post + (size_t)t0 * S, comb + (size_t)t0 * S * S,
+                    pre_lds);
+    }
+    lds_barrier();
+    // ---- collapse from registers
+    if (tok_ok) {
+      float pc[S];
+#pragma unroll
+      for (int c = 0; c < S; ++c) pc[c] = pre_lds[tq * 8 + c];
+      float* yt = y + (size_t)tok * H;
+#pragma unroll
+      for (int u = 0; u < CPW; ++u) {
+        const int h = 64 * (wave * CPW + u) + 4 * bq;
+        if (h < H) {
+          float4 xs[S];
+#pragma unroll
+          for (int c = 0; c < S; ++c) xs[c] = xr[c * CPW + u];
+          nt_store4(yt + h, collapse4<S>(pc, xs, S));
+        }
+      }
+    }
+    // the next tile's reduction reuses red / mr / pre_lds
+    lds_barrier();
+    have = want;
+  }
+}
+
 // Chunks per wave for a hidden size: ceil(H / 64 / 8), rounded up to a supported value.
 static int fused_cpw(int H) {
   const int need = (H + 64 * 8 - 1) / (64 * 8);
@@ -364,6 +585,20 @@ hipError_t launch_pack_weight(const float* fn_w, int S, int H, float* wpack, hip
   return hipErrorInvalidValue;
 }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int c = cached[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+
 hipError_t launch_fused_pre(const float* x, const float* fn_w, const float* scale,
                             const float* base, int T, int S, int H, int iters, float eps,
                             float* pre, float* post, float* comb, float* y, float* wpack,
@@ -384,6 +619,14 @@ hipError_t launch_fused_pre(const float* x, const float* fn_w, const float* scal
     if (!prepacked)                                                                           \
       hipLaunchKernelGGL((pack_weight_kernel<SS, (2 + SS) * SS, CC>),                         \
                          dim3((total + 255) / 256), dim3(256), 0, st, fn_w, H, pk);           \
+    if constexpr ((SS * CC) % 2 == 0 && SS * CC <= 32) {                                      \
+      const int cus = device_cus();                                                           \
+      if (!pin && !zq && cus > 0 && (T + 3) / 4 >= 4 * cus) {                                 \
+        hipLaunchKernelGGL((fused_pf_kernel<SS, CC>), dim3(cus), dim3(512), 0, st, x, pk,     \
+                           scale, base, T, H, iters, eps, pre, post, comb, y);                \
+        return hipGetLastError();                                                             \
+      }                                                                                       \
+    }                                                                                         \
     if (pin) {                                                                                \
       if (zq)                                                                                 \
         MHC_FK(SS, CC, true, true);                                                           \

@@ -50,8 +50,8 @@ def test_write_traffic_scales_by_the_copy_kernel(tmp_path, monkeypatch):
     _counter_db(fetch, "FETCH_SIZE", [
         (copy, 1 << 20, 131072.0),  # half of 256 MiB: the factor becomes 2
         ("void mhc::pack_weight_kernel<4, 24, 8>(float const*)", 98304, 800.0),
-        ("void mhc::fused_pre_kernel<4, 8, 1, false, false, false>(...)", 524288, 100000.0),
-        ("void mhc::fused_pre_kernel<4, 8, 1, false, false, false>(...)", 1024, 5.0),  # decode-size
+        ("void mhc::fused_pf_kernel<4, 8>(...)", 131072, 100000.0),
+        ("void mhc::fused_pf_kernel<4, 8>(...)", 512, 5.0),  # decode-size
         ("void mhc::post_kernel<4>(...)", 4194304, 160000.0),
         ("void mhc::fused_pre_kernel<4, 8, 1, false, true, false>(...)", 524288, 150000.0),
         ("void mhc::partials_kernel<5, 4>(...)", 131072, 210000.0),
@@ -60,8 +60,8 @@ def test_write_traffic_scales_by_the_copy_kernel(tmp_path, monkeypatch):
     _counter_db(write, "WRITE_SIZE", [
         (copy, 1 << 20, 262144.0),
         ("void mhc::pack_weight_kernel<4, 24, 8>(float const*)", 98304, 1536.0),
-        ("void mhc::fused_pre_kernel<4, 8, 1, false, false, false>(...)", 524288, 60000.0),
-        ("void mhc::fused_pre_kernel<4, 8, 1, false, false, false>(...)", 1024, 1.0),
+        ("void mhc::fused_pf_kernel<4, 8>(...)", 131072, 60000.0),
+        ("void mhc::fused_pf_kernel<4, 8>(...)", 512, 1.0),
         ("void mhc::post_kernel<4>(...)", 4194304, 262144.0),
         ("void mhc::fused_pre_kernel<4, 8, 1, false, true, false>(...)", 524288, 330000.0),
         ("void mhc::partials_kernel<5, 4>(...)", 131072, 12000.0),

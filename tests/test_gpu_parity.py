@@ -283,3 +283,29 @@ def test_largest_accepted_batch(mhc, S, H):
     del x, f, pre, post, comb, y, xo
     torch.cuda.empty_cache()
     check_site_with_oracle(xs, site, outs, 20, 1e-6, f"largest T{T}S{S}H{H}", x_out=xos)
+
+
+# ------------------------------------------------------------------ persistent tiles
+@pytest.mark.parametrize("S,H", [(4, 4096), (2, 8192), (3, 2048)])
+def test_persistent_tiles_match_the_fused_tiles_bit_for_bit(mhc, S, H):
+    """From four 4-token tiles per compute unit the pre chain runs on a
+    persistent grid that requests half of each next slab into LDS; smaller
+    batches (from 256 tokens) run one block per tile.  Both compute a tile the
+    same way, so the rows of one large batch equal, bit for bit, those of the
+    same tokens run in batches below the threshold (every batch a multiple of
+    four tokens, so the tiles line up, and at least 256 tokens, so none takes
+    the split path).  The batch ends on a ragged tile."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    step = 4 * cus                 # one tile per compute unit
+    T = 4 * step + 261             # four tiles per unit and more, ragged end
+    _say(f"persistent tiles T={T} S={S} H={H} ({cus} compute units)")
+    d = make_random_shape(T, S, H, seed=7000 + S)
+    whole = _run_pre(mhc, d, 20, 1e-6)
+    cuts = list(range(0, 4 * step + 1, step)) + [T]
+    parts = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        sub = {k: d[k][a:b] if k in ("x", "f") else d[k] for k in d}
+        parts.append(_run_pre(mhc, sub, 20, 1e-6))
+    for i, name in enumerate(("pre", "post", "comb", "y")):
+        joined = np.concatenate([p[i] for p in parts])
+        assert np.array_equal(whole[i], joined), f"{name} differs between the two schedules"
