@@ -33,12 +33,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                                                        int n, int R, int chunks_per_range,
                                                        float* __restrict__ part) {
   __shared__ float red[4 * block_slice<NRT, NTT>() * kWave];
-  const int g = blockIdx.y;
+  // Workgroups go to the eight XCDs in turn, by linear index.  When the
+  // K-range count is a multiple of eight, block L takes K-range
+  // g = L % 8 + 8 * ((L / 8) % (G / 8)) and token tile (L / 8) / (G / 8): each
+  // XCD then serves G / 8 K-ranges for every token tile, and its L2 fetches
+  // only those ranges of the weight.  A block's work does not depend on which
+  // block does it, so the results are the same either way.
+  int tile = blockIdx.x, g = blockIdx.y;
+  if ((gridDim.y & 7) == 0) {
+    const int L = blockIdx.y * gridDim.x + blockIdx.x;
+    const int gpx = gridDim.y >> 3;
+    const int r = L >> 3;
+    g = (L & 7) + 8 * (r % gpx);
+    tile = r / gpx;
+  }
   const int nchunks = (n + 15) >> 4;
   const int c_beg = g * chunks_per_range;
   const int c_end = min(nchunks, c_beg + chunks_per_range);
   float* pg = part + (size_t)g * T * (R + 1);
-  block_partials<NRT, NTT>(x, fn_w, T, n, R, blockIdx.x * (16 * NTT), c_beg, c_end, red,
+  block_partials<NRT, NTT>(x, fn_w, T, n, R, tile * (16 * NTT), c_beg, c_end, red,
                            [=](size_t i, float v) { pg[i] = v; });
 }
 
