@@ -1,7 +1,8 @@
 """HIP graph capture of whole sites: every replay equals the eager result bit for bit.
 
-Covers the three pre schedules (single-launch decode, split partials + finish,
-packed-weight fused tiles) and the post kernel.  Every replay is also compared
+Covers the pre schedules (single-launch decode, split partials + finish,
+packed-weight fused tiles, and at the prefill chunk the persistent tiles that
+request half of each next slab into LDS) and the post kernel.  Every replay is also compared
 with the fp64 oracle on every token.  Between replays the program
 runs its own eager work (a different site through the same library scratch)
 and synchronises, so a replay that depended on state left by the capture, or
