@@ -382,11 +382,43 @@ __global__ __launch_bounds__(512) void fused_pf_kernel(
   const int n = S * H;
   const int ntiles = (T + 3) / 4;
 
+  float4 xr[NCH];
+  float4 wb[WD + 1][RG];
+  // A tile's slab (buffer loads straight into xr: lanes whose slab is in LDS,
+  // and tokens past T, are out of range and fetch nothing) and its first
+  // weight chunk.  Lane values come from an opaque copy of the thread index,
+  // as everywhere in the tile loop: they are the same in every tile, and kept
+  // across it they would hold registers the slab needs.
+  auto request_tile = [&](int tile, bool in_lds) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & (kWave - 1);
+    const int wave = tid >> 6;
+    const int tq = lane >> 4, bq = lane & 15;
+    const int hb = 64 * wave * CPW + 4 * bq, tb = tq * n;
+    const int wo = wave * NCH * RG * 64 + lane;
+    const int t0 = tile * 4;
+    const bool skip = in_lds && tq >= 2;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(x + (size_t)t0 * n), (short)0, min(4, T - t0) * n * 4, 0x00020000);
+#pragma unroll
+    for (int ci = 0; ci < NCH; ++ci) {
+      const int c = ci / CPW, u = ci % CPW;
+      const int h = hb + 64 * u;
+      const int off = skip ? 0x7FFFFFF0 : 4 * (tb + c * H + (h < H ? h : 0));
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2);
+      xr[ci] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                           __uint_as_float(v[3]));
+    }
+#pragma unroll
+    for (int ci = 0; ci < WD && ci < NCH; ++ci)
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) wb[ci][rg] = wpack[wo + (ci * RG + rg) * 64];
+  };
+
   bool have = false;  // tokens 2 and 3 of this tile are in LDS (the same in every lane)
+  if (blockIdx.x < ntiles) request_tile(blockIdx.x, false);
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    // Every lane-dependent value is derived from an opaque copy of the thread
-    // index in each tile: the values are the same in every tile, and kept
-    // across the tile loop they would hold registers the slab needs.
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int lane = tid & (kWave - 1);
@@ -398,48 +430,32 @@ __global__ __launch_bounds__(512) void fused_pf_kernel(
     // this lane's record entry for chunk ci (lanes of tokens 0 and 1 read an
     // entry of token 2, which they discard)
     const int rec_lane = 16 * ((tq - 2) & 1) + bq;
-    const int hb = 64 * wave * CPW + 4 * bq, tb = tq * n;
+    const int hb = 64 * wave * CPW + 4 * bq;
     const int t0 = tile * 4;
     const int tok = t0 + tq;
     const bool tok_ok = tok < T;
     const int next = tile + gridDim.x;
     const bool want = next < ntiles;  // the same in every lane
-
-    // ---- the tile's slab: buffer loads straight into xr (lanes whose slab is
-    // in LDS, and tokens past T, are out of range and fetch nothing); the
-    // record entries replace those lanes' values as each chunk is consumed
     const bool use_lds = have && tq >= 2;
-    const int valid = min(4, T - t0);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(x + (size_t)t0 * n), (short)0, valid * n * 4, 0x00020000);
-    float4 xr[NCH];
-#pragma unroll
-    for (int ci = 0; ci < NCH; ++ci) {
-      const int c = ci / CPW, u = ci % CPW;
-      const int h = hb + 64 * u;
-      const int off = use_lds ? 0x7FFFFFF0 : 4 * (tb + c * H + (h < H ? h : 0));
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2);
-      xr[ci] = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
-                           __uint_as_float(v[3]));
-    }
 
-    // ---- weight stream and MFMAs, as in fused_pre_kernel
+    // The slab and the first weight chunk, requested at the end of the
+    // previous tile (or above), and the request into LDS issued before them
+    // have landed before any record is read.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- weight stream and MFMAs, as in fused_pre_kernel; the record entries
+    // replace the slab values of lanes whose slab is in LDS as each chunk is
+    // consumed
     floatx4 acc[RG];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) acc[rg] = floatx4{0.f, 0.f, 0.f, 0.f};
     float ss = 0.f;
-    float4 wb[WD + 1][RG];
     auto load_w = [&](int ci, float4* dst) {
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) dst[rg] = wpack[wo + (ci * RG + rg) * 64];
     };
-#pragma unroll
-    for (int ci = 0; ci < WD && ci < NCH; ++ci) load_w(ci, wb[ci]);
-    // The request from the previous tile (issued before this tile's own loads,
-    // so complete once they are) has landed before any record is read.
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ci = 0; ci < NCH; ++ci) {
       if (ci + WD < NCH) load_w(ci + WD, wb[(ci + WD) % (WD + 1)]);
@@ -493,7 +509,7 @@ __global__ __launch_bounds__(512) void fused_pf_kernel(
       }
     }
 
-    // ---- fixed-order reduction, gates, Sinkhorn (as in fused_pre_kernel)
+    // ---- fixed-order reduction (as in fused_pre_kernel)
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
@@ -514,18 +530,14 @@ __global__ __launch_bounds__(512) void fused_pf_kernel(
       mr[o / (R + 1)][o % (R + 1)] = sum;
     }
     lds_barrier();
-    if (wave == 0) {
-      const int ntok = min(4, T - t0);
-      gates_wave<4, true, true>(&mr[0][0], R + 1, ntok, S, n, params, iters, eps, true,
-                    pre + (size_t)t0 * S, post + (size_t)t0 * S, comb + (size_t)t0 * S * S,
-                    pre_lds);
-    }
-    lds_barrier();
-    // ---- collapse from registers
+
+    // ---- collapse from registers, each lane taking its token's pre gates
+    // from the sums with the pre-gate routine gates_wave uses (so the two
+    // agree to the bit); the Sinkhorn is not on this path
     if (tok_ok) {
       float pc[S];
 #pragma unroll
-      for (int c = 0; c < S; ++c) pc[c] = pre_lds[tq * 8 + c];
+      for (int c = 0; c < S; ++c) pc[c] = pre_gate(&mr[tq][0], c, R, n, eps, params);
       float* yt = y + (size_t)tok * H;
 #pragma unroll
       for (int u = 0; u < CPW; ++u) {
@@ -538,7 +550,16 @@ __global__ __launch_bounds__(512) void fused_pf_kernel(
         }
       }
     }
-    // the next tile's reduction reuses red / mr / pre_lds
+    // ---- the next tile's slab (its tokens 2 and 3 are on their way into
+    // LDS) streams in while wave 0 runs the gates and the Sinkhorn
+    if (want) request_tile(next, true);
+    if (wave == 0) {
+      const int ntok = min(4, T - t0);
+      gates_wave<4, true, true>(&mr[0][0], R + 1, ntok, S, n, params, iters, eps, true,
+                                pre + (size_t)t0 * S, post + (size_t)t0 * S,
+                                comb + (size_t)t0 * S * S, pre_lds);
+    }
+    // the next tile's reduction reuses red and mr
     lds_barrier();
     have = want;
   }
