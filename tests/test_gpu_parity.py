@@ -286,7 +286,7 @@ def test_largest_accepted_batch(mhc, S, H):
 
 
 # ------------------------------------------------------------------ persistent tiles
-@pytest.mark.parametrize("S,H", [(4, 4096), (2, 8192), (3, 2048)])
+@pytest.mark.parametrize("S,H", [(4, 4096), (2, 8192), (3, 2048), (4, 4000), (1, 1100)])
 def test_persistent_tiles_match_the_fused_tiles_bit_for_bit(mhc, S, H):
     """From four 4-token tiles per compute unit the pre chain runs on a
     persistent grid that requests half of each next slab into LDS; smaller
@@ -294,7 +294,9 @@ def test_persistent_tiles_match_the_fused_tiles_bit_for_bit(mhc, S, H):
     same way, so the rows of one large batch equal, bit for bit, those of the
     same tokens run in batches below the threshold (every batch a multiple of
     four tokens, so the tiles line up, and at least 256 tokens, so none takes
-    the split path).  The batch ends on a ragged tile."""
+    the split path).  The batch ends on a ragged tile; H = 4000 and 1100 leave
+    the last chunks of some waves past the hidden size.  The whole batch is
+    also checked against the oracle, every token."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     step = 4 * cus                 # one tile per compute unit
     T = 4 * step + 261             # four tiles per unit and more, ragged end
@@ -309,3 +311,4 @@ def test_persistent_tiles_match_the_fused_tiles_bit_for_bit(mhc, S, H):
     for i, name in enumerate(("pre", "post", "comb", "y")):
         joined = np.concatenate([p[i] for p in parts])
         assert np.array_equal(whole[i], joined), f"{name} differs between the two schedules"
+    check_site_with_oracle(d["x"], d, list(whole), 20, 1e-6, f"persistent T{T}S{S}H{H}")
