@@ -27,7 +27,7 @@ namespace mhc {
 
 // Two waves per SIMD at least: the register bound keeps the three operand sets
 // of the chunk loop from dropping the kernel to one wave per SIMD.
-template <int NRT, int NTT>
+template <int NRT, int NTT, bool BUF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void partials_kernel(const float* __restrict__ x,
                                                        const float* __restrict__ fn_w, int T,
                                                        int n, int R, int chunks_per_range,
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int c_beg = g * chunks_per_range;
   const int c_end = min(nchunks, c_beg + chunks_per_range);
   float* pg = part + (size_t)g * T * (R + 1);
-  block_partials<NRT, NTT>(x, fn_w, T, n, R, tile * (16 * NTT), c_beg, c_end, red,
+  block_partials<NRT, NTT, BUF>(x, fn_w, T, n, R, tile * (16 * NTT), c_beg, c_end, red,
                            [=](size_t i, float v) { pg[i] = v; });
 }
 
@@ -59,8 +59,15 @@ template <int NRT, int NTT>
 static hipError_t launch_partials_t(const float* x, const float* fn_w, int T, int n, int R,
                                     int G, int chunks_per_range, float* part, hipStream_t st) {
   dim3 grid((T + 16 * NTT - 1) / (16 * NTT), G);
-  hipLaunchKernelGGL((partials_kernel<NRT, NTT>), grid, dim3(256), 0, st, x, fn_w, T, n, R,
-                     chunks_per_range, part);
+  // buffer loads where every byte offset of a block's rows and tokens fits in
+  // 31 bits
+  const long rows = 16L * (NRT > NTT ? NRT : NTT);
+  if (rows * n * 4 + 64 < (1L << 31))
+    hipLaunchKernelGGL((partials_kernel<NRT, NTT, true>), grid, dim3(256), 0, st, x, fn_w, T, n,
+                       R, chunks_per_range, part);
+  else
+    hipLaunchKernelGGL((partials_kernel<NRT, NTT, false>), grid, dim3(256), 0, st, x, fn_w, T,
+                       n, R, chunks_per_range, part);
   return hipGetLastError();
 }
 

@@ -48,7 +48,7 @@ constexpr int block_slice() {
   return (block_vals<NRT, NTT>() + block_passes<NRT, NTT>() - 1) / block_passes<NRT, NTT>();
 }
 
-template <int NRT, int NTT, class Sink>
+template <int NRT, int NTT, bool BUF, class Sink>
 __device__ __forceinline__ void block_partials(const float* __restrict__ x,
                                                const float* __restrict__ fn_w, int T, int n,
                                                int R, int tok0, int c_beg, int c_end,
@@ -71,49 +71,87 @@ __device__ __forceinline__ void block_partials(const float* __restrict__ x,
   const int sub = lane & 15;       // row within a row tile / token within a token tile
   const int kq = (lane >> 4) * 4;  // this lane's 4-float offset inside a 16-float chunk
 
-  // Row and token pointers, clamped to a valid row / token: out-of-range lanes
-  // read valid memory and are zeroed before use.
+  // BUF: operands through buffer loads, one resource over the R weight rows
+  // and one over the block's tokens in range, so lanes of rows past R or
+  // tokens past T read zero (out of range), and a chunk past the slab takes an
+  // out-of-range offset: no select in the chunk loop.  The launch takes this
+  // form when every byte offset fits in 31 bits.  Otherwise row and token
+  // pointers are clamped to a valid row / token, and the out-of-range lanes
+  // are zeroed by a select when the chunk is consumed.
   const float* wrow[NRT];
   bool wvalid[NRT];
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    const int r = rt * 16 + sub;
-    wvalid[rt] = r < R;
-    wrow[rt] = fn_w + (size_t)(wvalid[rt] ? r : 0) * n;
-  }
   const float* xrow[NTT];
   bool xvalid[NTT];
+  int woff[NRT], xoff[NTT];  // byte offsets of this lane's rows and tokens (BUF)
+  __amdgpu_buffer_rsrc_t wrs, xrs;
+  if constexpr (BUF) {
+    wrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(fn_w), (short)0, R * n * 4,
+                                            0x00020000);
+    const int tv = T - tok0 < 16 * NTT ? T - tok0 : 16 * NTT;  // the block's tokens in range
+    xrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(x + (size_t)tok0 * n), (short)0,
+                                            tv * n * 4, 0x00020000);
 #pragma unroll
-  for (int tt = 0; tt < NTT; ++tt) {
-    const int t = tok0 + tt * 16 + sub;
-    xvalid[tt] = t < T;
-    xrow[tt] = x + (size_t)(xvalid[tt] ? t : 0) * n;
+    for (int rt = 0; rt < NRT; ++rt) woff[rt] = (rt * 16 + sub) * n * 4;
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) xoff[tt] = (tt * 16 + sub) * n * 4;
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      const int r = rt * 16 + sub;
+      wvalid[rt] = r < R;
+      wrow[rt] = fn_w + (size_t)(wvalid[rt] ? r : 0) * n;
+    }
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) {
+      const int t = tok0 + tt * 16 + sub;
+      xvalid[tt] = t < T;
+      xrow[tt] = x + (size_t)(xvalid[tt] ? t : 0) * n;
+    }
   }
 
   // Chunk loop over three operand sets: the loads of chunk c + 8 are issued
   // before the MFMAs of chunk c, so two chunks are in flight behind the one
-  // being consumed.  Loads are branch-free (clamped addresses) and the
-  // out-of-range lanes are zeroed by a select when the chunk is consumed.
+  // being consumed.  Loads are branch-free.
+  auto ld = [](__amdgpu_buffer_rsrc_t rs, int off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                       __uint_as_float(v[3]));
+  };
   auto load_chunk = [&](int c, float4* a, float4* b) {
     const int k = c * 16 + kq;
-    const int kc = k < n ? k : 0;
+    if constexpr (BUF) {
+      const bool kin = k < n;  // n % 4 == 0: a float4 is fully in or fully out
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) a[rt] = *reinterpret_cast<const float4*>(wrow[rt] + kc);
+      for (int rt = 0; rt < NRT; ++rt) a[rt] = ld(wrs, kin ? woff[rt] + 4 * k : 0x7FFFFFF0);
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) b[tt] = *reinterpret_cast<const float4*>(xrow[tt] + kc);
+      for (int tt = 0; tt < NTT; ++tt) b[tt] = ld(xrs, kin ? xoff[tt] + 4 * k : 0x7FFFFFF0);
+    } else {
+      const int kc = k < n ? k : 0;
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) a[rt] = *reinterpret_cast<const float4*>(wrow[rt] + kc);
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) b[tt] = *reinterpret_cast<const float4*>(xrow[tt] + kc);
+    }
   };
   auto sel = [](bool ok, float4 v) {
     return make_float4(ok ? v.x : 0.f, ok ? v.y : 0.f, ok ? v.z : 0.f, ok ? v.w : 0.f);
   };
-  // The MFMAs of one chunk, on operands a0 / b0 (zeroed outside the valid
-  // rows, tokens and K).
+  // The MFMAs of one chunk, on operands a0 / b0 (zero outside the valid rows,
+  // tokens and K).
   auto consume = [&](int c, const float4* a0, const float4* b0) {
-    const bool kin = c * 16 + kq < n;  // n % 4 == 0: a float4 is fully in or fully out
     float4 a[NRT], b[NTT];
+    if constexpr (BUF) {
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) a[rt] = sel(kin && wvalid[rt], a0[rt]);
+      for (int rt = 0; rt < NRT; ++rt) a[rt] = a0[rt];
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) b[tt] = sel(kin && xvalid[tt], b0[tt]);
+      for (int tt = 0; tt < NTT; ++tt) b[tt] = b0[tt];
+    } else {
+      const bool kin = c * 16 + kq < n;  // n % 4 == 0: a float4 is fully in or fully out
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) a[rt] = sel(kin && wvalid[rt], a0[rt]);
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) b[tt] = sel(kin && xvalid[tt], b0[tt]);
+    }
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
       ss[tt] = fmaf(b[tt].x, b[tt].x, ss[tt]);
@@ -143,7 +181,8 @@ __device__ __forceinline__ void block_partials(const float* __restrict__ x,
         acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[rt].w, b[tt].w, acc[rt][tt], 0, 0, 0);
   };
   // three operand sets in a ring: chunk c + 8 is requested while chunk c is
-  // consumed (the ring is unrolled so every set stays in named registers)
+  // consumed (the ring is unrolled so every set stays in named registers; a
+  // fourth set measured slower in the buffer form)
   float4 a0[NRT], b0[NTT], a1[NRT], b1[NTT], a2[NRT], b2[NTT];
   int c = c_beg + wave;
   if (c < c_end) load_chunk(c, a0, b0);
