@@ -645,7 +645,7 @@ TRAFFIC_UNITS = {
     "pre_call": ["pack_weight_kernel<4, 24, 8>", "fused_pf_kernel<4, 8>"],
     "post_kernel": ["post_kernel<4>"],
     "walk_call": ["pack_weight_kernel<4, 24, 8>", "fused_pre_kernel<4, 8, 1, false, true, false>"],
-    "wide_pre_call": ["partials_kernel<5, 4>", "finish_kernel<8>"],
+    "wide_pre_call": ["partials_kernel<5, 4, true>", "finish_kernel<8>"],
     "wide_post_kernel": ["post_kernel<8>"],
 }
 

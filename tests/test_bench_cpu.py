@@ -54,7 +54,7 @@ def test_write_traffic_scales_by_the_copy_kernel(tmp_path, monkeypatch):
         ("void mhc::fused_pf_kernel<4, 8>(...)", 512, 5.0),  # decode-size
         ("void mhc::post_kernel<4>(...)", 4194304, 160000.0),
         ("void mhc::fused_pre_kernel<4, 8, 1, false, true, false>(...)", 524288, 150000.0),
-        ("void mhc::partials_kernel<5, 4>(...)", 131072, 210000.0),
+        ("void mhc::partials_kernel<5, 4, true>(...)", 131072, 210000.0),
         ("void mhc::finish_kernel<8>(...)", 262144, 120000.0),
         ("void mhc::post_kernel<8>(...)", 1835008, 130000.0)])
     _counter_db(write, "WRITE_SIZE", [
@@ -64,7 +64,7 @@ def test_write_traffic_scales_by_the_copy_kernel(tmp_path, monkeypatch):
         ("void mhc::fused_pf_kernel<4, 8>(...)", 512, 1.0),
         ("void mhc::post_kernel<4>(...)", 4194304, 262144.0),
         ("void mhc::fused_pre_kernel<4, 8, 1, false, true, false>(...)", 524288, 330000.0),
-        ("void mhc::partials_kernel<5, 4>(...)", 131072, 12000.0),
+        ("void mhc::partials_kernel<5, 4, true>(...)", 131072, 12000.0),
         ("void mhc::finish_kernel<8>(...)", 262144, 29000.0),
         ("void mhc::post_kernel<8>(...)", 1835008, 229376.0)])
     out = tmp_path / "traffic.json"
