@@ -112,3 +112,23 @@ def test_fit_line_matches_least_squares():
         bench.fit_line([1], [2.0])
     with pytest.raises(ValueError):
         bench.fit_line([2, 2], [1.0, 3.0])
+
+
+def test_traffic_units_name_kernels_that_exist():
+    """Every kernel named in the traffic table is a __global__ template in the
+    library sources with that many template arguments, so a renamed or
+    re-templated kernel fails here rather than as a missing counter row on the
+    GPU machine."""
+    import glob
+    import re
+    src = "".join(open(p).read() for p in
+                  glob.glob(os.path.join(ROOT, "mhc_hyper_connection_token_amd", "csrc", "*.hip")))
+    kernels = {}
+    for m in re.finditer(r"template\s*<([^>]*)>\s*__global__[^;{]*?\bvoid\s+(\w+)\s*\(", src):
+        kernels[m.group(2)] = len([a for a in m.group(1).split(",") if a.strip()])
+    for unit, names in bench.TRAFFIC_UNITS.items():
+        for nm in names:
+            base, _, args = nm.partition("<")
+            assert base in kernels, f"{unit}: no kernel named {base}"
+            nargs = len([a for a in args.rstrip(">").split(",") if a.strip()])
+            assert nargs == kernels[base], f"{unit}: {nm} has {nargs} template arguments"
