@@ -327,7 +327,7 @@ __global__ __launch_bounds__(512) void fused_pre_kernel(
 
 // ---------------------------------------------------------------- persistent tiles
 // The same token-tiled pre chain (fused_pre_kernel without the epilogue, the
-// post half or the head) on a persistent grid, for batches of four tiles or
+// post half or the head) on a persistent grid, for batches of two tiles or
 // more per compute unit: block b takes tiles b, b + G, b + 2G, ..., and after
 // a tile's last MFMA it requests tokens 2 and 3 of its next tile into LDS, so
 // that half of the next slab streams in while this tile reduces its partial
@@ -642,7 +642,7 @@ hipError_t launch_fused_pre(const float* x, const float* fn_w, const float* scal
                          dim3((total + 255) / 256), dim3(256), 0, st, fn_w, H, pk);           \
     if constexpr ((SS * CC) % 2 == 0 && SS * CC <= 32) {                                      \
       const int cus = device_cus();                                                           \
-      if (!pin && !zq && cus > 0 && (T + 3) / 4 >= 4 * cus) {                                 \
+      if (!pin && !zq && cus > 0 && (T + 3) / 4 >= 2 * cus) {                                 \
         hipLaunchKernelGGL((fused_pf_kernel<SS, CC>), dim3(cus), dim3(512), 0, st, x, pk,     \
                            scale, base, T, H, iters, eps, pre, post, comb, y);                \
         return hipGetLastError();                                                             \

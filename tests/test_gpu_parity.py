@@ -288,7 +288,7 @@ def test_largest_accepted_batch(mhc, S, H):
 # ------------------------------------------------------------------ persistent tiles
 @pytest.mark.parametrize("S,H", [(4, 4096), (2, 8192), (3, 2048), (4, 4000), (1, 1100)])
 def test_persistent_tiles_match_the_fused_tiles_bit_for_bit(mhc, S, H):
-    """From four 4-token tiles per compute unit the pre chain runs on a
+    """From two 4-token tiles per compute unit the pre chain runs on a
     persistent grid that requests half of each next slab into LDS; smaller
     batches (from 256 tokens) run one block per tile.  Both compute a tile the
     same way, so the rows of one large batch equal, bit for bit, those of the
@@ -299,7 +299,7 @@ def test_persistent_tiles_match_the_fused_tiles_bit_for_bit(mhc, S, H):
     also checked against the oracle, every token."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     step = 4 * cus                 # one tile per compute unit
-    T = 4 * step + 261             # four tiles per unit and more, ragged end
+    T = 4 * step + 261             # over four tiles per unit, ragged end
     _say(f"persistent tiles T={T} S={S} H={H} ({cus} compute units)")
     d = make_random_shape(T, S, H, seed=7000 + S)
     whole = _run_pre(mhc, d, 20, 1e-6)
