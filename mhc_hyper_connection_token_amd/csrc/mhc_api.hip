@@ -281,7 +281,7 @@ int site_pre_run(const float* x, const float* fn_w, const float* scale, const fl
     } else {
       // S <= 4 below the fused threshold: the vector-ALU partials
       e = (S <= 4 && T < kFusedMinTokens)
-              ? mhc::launch_small_partials(x, fn_w, T, S, H, p.G, p.cpr, part, st)
+              ? mhc::launch_small_partials(x, fn_w, T, S, H, p.G, p.cpr, part, st, scale, base)
               : mhc::launch_partials(x, fn_w, T, n, R, p.ntt, p.G, p.cpr, part, st);
       if (e == hipSuccess)
         e = mhc::launch_finish(x, part, p.G, T, S, H, scale, base, iters, eps, pre, post, comb,

@@ -186,41 +186,49 @@ __device__ __forceinline__ void stage_site_params(const float* __restrict__ scal
 //   pre_lds      : pre gates for the collapse, slot u at + u*8.
 // Per token: rinv = 1/sqrt(ss/n + eps); m = raw*rinv; z = fma(scale_g, m, base);
 // pre = sigmoid(z), post = 2 sigmoid(z), comb = Sinkhorn(exp(z)).
+// The two halves, gates_pre_post and gates_comb, may also run on two different
+// wavefronts (same arguments); gates_comb needs all 64 lanes of its wave.
 template <int L, bool PRE = true, bool POST_NT = false>
-__device__ __forceinline__ void gates_wave(const float* mraw, int ldm, int ntok, int S, int n,
-                                           const float* params, int iters, float eps,
-                                           bool write_out, float* __restrict__ pre,
-                                           float* __restrict__ post, float* __restrict__ comb,
-                                           float* pre_lds) {
+__device__ __forceinline__ void gates_pre_post(const float* mraw, int ldm, int ntok, int S,
+                                               int n, const float* params, float eps,
+                                               bool write_out, float* __restrict__ pre,
+                                               float* __restrict__ post, float* pre_lds) {
   const int lane = threadIdx.x & (kWave - 1);
   const int R = (2 + S) * S;
-  const float s_post = params[1], s_comb = params[2];
+  const float s_post = params[1];
   const float* base = params + 3;
-  // pre / post: lane = 8*u + g (g < 2S) for L = 4; lane = g for L = 8
-  {
-    const int u = (L == 4) ? (lane >> 3) : 0;
-    const int g = (L == 4) ? (lane & 7) : lane;
-    if (u < ntok && g < 2 * S && (L == 8 || lane < 32)) {
-      const float* mr = mraw + u * ldm;
-      if (g < S) {
-        if (PRE) {
-          const float v = pre_gate(mr, g, R, n, eps, params);
-          if (write_out) pre[u * S + g] = v;
-          pre_lds[u * 8 + g] = v;
-        }
-      } else {
-        const float rinv = rms_inverse(mr[R], n, eps);
-        const float v = 2.0f * sigmoid_exact_ends(fmaf(s_post, mr[g] * rinv, base[g]));
-        if (write_out) {
-          if (POST_NT)
-            __builtin_nontemporal_store(v, post + u * S + g - S);
-          else
-            post[u * S + g - S] = v;
-        }
+  // lane = 8*u + g (g < 2S) for L = 4; lane = g for L = 8
+  const int u = (L == 4) ? (lane >> 3) : 0;
+  const int g = (L == 4) ? (lane & 7) : lane;
+  if (u < ntok && g < 2 * S && (L == 8 || lane < 32)) {
+    const float* mr = mraw + u * ldm;
+    if (g < S) {
+      if (PRE) {
+        const float v = pre_gate(mr, g, R, n, eps, params);
+        if (write_out) pre[u * S + g] = v;
+        pre_lds[u * 8 + g] = v;
+      }
+    } else {
+      const float rinv = rms_inverse(mr[R], n, eps);
+      const float v = 2.0f * sigmoid_exact_ends(fmaf(s_post, mr[g] * rinv, base[g]));
+      if (write_out) {
+        if (POST_NT)
+          __builtin_nontemporal_store(v, post + u * S + g - S);
+        else
+          post[u * S + g - S] = v;
       }
     }
   }
-  // comb
+}
+
+template <int L>
+__device__ __forceinline__ void gates_comb(const float* mraw, int ldm, int ntok, int S, int n,
+                                           const float* params, int iters, float eps,
+                                           bool write_out, float* __restrict__ comb) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int R = (2 + S) * S;
+  const float s_comb = params[2];
+  const float* base = params + 3;
   int j, k, u;
   sinkhorn_lane_entry<L>(lane, u, j, k);
   const bool valid = (j < S) && (k < S) && (u < ntok);
@@ -233,6 +241,17 @@ __device__ __forceinline__ void gates_wave(const float* mraw, int ldm, int ntok,
   }
   c = sinkhorn_lanes<L>(c, iters, eps);
   if (valid && write_out) comb[u * S * S + j * S + k] = c;
+}
+
+template <int L, bool PRE = true, bool POST_NT = false>
+__device__ __forceinline__ void gates_wave(const float* mraw, int ldm, int ntok, int S, int n,
+                                           const float* params, int iters, float eps,
+                                           bool write_out, float* __restrict__ pre,
+                                           float* __restrict__ post, float* __restrict__ comb,
+                                           float* pre_lds) {
+  gates_pre_post<L, PRE, POST_NT>(mraw, ldm, ntok, S, n, params, eps, write_out, pre, post,
+                                  pre_lds);
+  gates_comb<L>(mraw, ldm, ntok, S, n, params, iters, eps, write_out, comb);
 }
 
 // y = sum_c pre[c] * x_c, streams in ascending order, first term a product.

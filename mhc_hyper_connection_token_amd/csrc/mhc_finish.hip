@@ -7,11 +7,14 @@
 // collapse the streams: y[t,i] = sum_c pre[t,c] * x[t,c,i].
 //
 // Grid: (T, HB).  Block y-index hb covers a contiguous range of hidden quads
-// for the collapse; every block of a token recomputes the (cheap) pre gates so
-// that no cross-block wait is needed, and only hb == 0 runs the Sinkhorn and
-// writes pre/post/comb.  The
-// first x quads of the collapse are loaded before the gates are computed, so
-// their latency hides behind the reduction and the Sinkhorn.
+// for the collapse; every thread that collapses computes the (cheap) pre gates
+// itself, so that no cross-block wait is needed.  In block hb == 0, wave 0
+// runs the comb gates and the Sinkhorn while wave 3 writes pre and post.  Wave 0
+// takes the last quads of each 256, so that where a block has at most 192
+// quads (small T) the Sinkhorn wave does no collapse work.  Blocks with more
+// than one pass of quads request their first collapse operands before the
+// reduction, to hide that latency; single-pass blocks request them after it,
+// so that the reduction does not wait behind them (loads complete in order).
 #include "mhc_kernels.h"
 #include "mhc_split.h"
 
@@ -31,45 +34,46 @@ __global__ __launch_bounds__(256) void finish_kernel(
   __shared__ float red[256];
   __shared__ float m_raw[96];
   __shared__ float params[3 + 80];
+  __shared__ float pre_lds[8];
   stage_site_params(scale, base, R, params);
 
-  // 0. first collapse quad of this thread, loaded early
   const int q0 = hb * quads_per_block;
   const int q1 = min(HQ, q0 + quads_per_block);
+  const bool early = q1 - q0 > 256;  // block-uniform
   const float4* xt = reinterpret_cast<const float4*>(x + (size_t)t * S * H);
+  const int qa = q0 + ((threadIdx.x + 192) & 255);
   float4 xq[8];
-  const int qa = q0 + threadIdx.x;
-  if (qa < q1) {
+  auto load_quads = [&](int q) {
 #pragma unroll
     for (int c = 0; c < 8; ++c)
-      if (c < S) xq[c] = xt[(size_t)c * HQ + qa];
-  }
+      if (c < S) xq[c] = xt[(size_t)c * HQ + q];
+  };
+  if (early && qa < q1) load_quads(qa);
 
   // 1. fixed-order reduction of the G partials
   reduce_token_partials<false, 16>(part, G, T, t, RP, red, m_raw);
 
-  // 2. pre gates, computed by every thread (uniform); only block hb == 0 runs
-  // the Sinkhorn (wave 0, post and comb) and writes the gates.  No barrier
-  // follows, so the other waves collapse while wave 0 iterates.
-  float pc[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) pc[c] = c < S ? pre_gate(m_raw, c, R, S * H, eps, params) : 0.f;
+  // 2. block 0: comb (gates and Sinkhorn) on wave 0, pre and post on wave 3
   if (hb == 0) {
-    if (threadIdx.x < S)
-      pre[(size_t)t * S + threadIdx.x] = pre_gate(m_raw, threadIdx.x, R, S * H, eps, params);
     if (threadIdx.x < kWave)
-      gates_wave<L, false>(m_raw, 0, 1, S, S * H, params, iters, eps, true, nullptr,
-                           post + (size_t)t * S, comb + (size_t)t * S * S, nullptr);
+      gates_comb<L>(m_raw, 0, 1, S, S * H, params, iters, eps, true, comb + (size_t)t * S * S);
+    else if (threadIdx.x >= 3 * kWave)
+      gates_pre_post<L>(m_raw, 0, 1, S, S * H, params, eps, true, pre + (size_t)t * S,
+                        post + (size_t)t * S, pre_lds);
   }
 
   // 3. collapse
-  float4* yt = reinterpret_cast<float4*>(y + (size_t)t * H);
-  if (qa < q1) yt[qa] = collapse4<8>(pc, xq, S);
-  for (int q = qa + 256; q < q1; q += 256) {
+  if (qa < q1) {
+    if (!early) load_quads(qa);
+    float pc[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      if (c < S) xq[c] = xt[(size_t)c * HQ + q];
-    yt[q] = collapse4<8>(pc, xq, S);
+    for (int c = 0; c < 8; ++c) pc[c] = c < S ? pre_gate(m_raw, c, R, S * H, eps, params) : 0.f;
+    float4* yt = reinterpret_cast<float4*>(y + (size_t)t * H);
+    yt[qa] = collapse4<8>(pc, xq, S);
+    for (int q = qa + 256; q < q1; q += 256) {
+      load_quads(q);
+      yt[q] = collapse4<8>(pc, xq, S);
+    }
   }
 }
 

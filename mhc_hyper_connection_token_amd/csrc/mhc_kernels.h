@@ -20,13 +20,17 @@ hipError_t launch_partials(const float* x, const float* fn_w, int T, int n, int 
                            int G, int chunks_per_range, float* part, hipStream_t st);
 
 // Vector-ALU split-K partials (S <= 4, any T in groups of 16 tokens), per token
-// in the order the single-launch decode kernel uses; same part layout.
+// in the order the single-launch decode kernel uses; same part layout.  With
+// scale / base given, one block also reads the site parameters first thing, so
+// that the finish kernel finds them in the memory-side cache.
 int small_rows_per_thread(int S);
 hipError_t launch_small_partials(const float* x, const float* fn_w, int T, int S, int H, int G,
-                                 int chunks_per_range, float* part, hipStream_t st);
+                                 int chunks_per_range, float* part, hipStream_t st,
+                                 const float* scale = nullptr, const float* base = nullptr);
 // The same for any R <= 31 rows of a weight [R][n] (the head's R = S).
 hipError_t launch_small_partials_rows(const float* x, const float* fn_w, int T, int n, int R,
-                                      int G, int chunks_per_range, float* part, hipStream_t st);
+                                      int G, int chunks_per_range, float* part, hipStream_t st,
+                                      const float* scale = nullptr, const float* base = nullptr);
 
 // Reduce partials, gates, Sinkhorn, collapse.
 hipError_t launch_finish(const float* x, const float* part, int G, int T, int S, int H,
