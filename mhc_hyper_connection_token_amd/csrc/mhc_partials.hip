@@ -99,7 +99,9 @@ struct ParamTouch {
   __device__ __forceinline__ void consume() const { asm volatile("" ::"v"(v)); }
 };
 
-template <int RPT, int QL>
+// TG tokens per group: kSmallGroup, or 1 for a single token (the same sums,
+// since every partial is its own lane tree, with a quarter of the work).
+template <int RPT, int QL, int TG>
 __global__ __launch_bounds__(256) void small_partials_kernel(const float* __restrict__ x,
                                                              const float* __restrict__ fn_w,
                                                              int T, int n, int R,
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(256) void small_partials_kernel(const float* __rest
   const int k_beg = g * chunks_per_range * 16;
   const int k_end = min(n, k_beg + chunks_per_range * 16);
   float* pg = part + (size_t)g * T * (R + 1);
-  small_partials_groups<kSmallGroup, RPT, QL>(
+  small_partials_groups<TG, RPT, QL>(
       x, fn_w, T, n, R, k_beg, k_end, blockIdx.y, gridDim.y,
       [=](int t, int r, float v) {
         touch.consume();
@@ -168,8 +170,12 @@ hipError_t launch_small_partials_rows(const float* x, const float* fn_w, int T, 
   const int rpt = rows_per_thread(R);
 #define MHC_SP(RP_, QL_)                                                                       \
   if (rpt == RP_ && ql <= QL_) {                                                               \
-    hipLaunchKernelGGL((small_partials_kernel<RP_, QL_>), grid, dim3(256), 0, st, x, fn_w, T, n, \
-                       R, chunks_per_range, part, scale, base);                                \
+    if (T == 1)                                                                                \
+      hipLaunchKernelGGL((small_partials_kernel<RP_, QL_, 1>), grid, dim3(256), 0, st, x, fn_w, \
+                         T, n, R, chunks_per_range, part, scale, base);                        \
+    else                                                                                       \
+      hipLaunchKernelGGL((small_partials_kernel<RP_, QL_, kSmallGroup>), grid, dim3(256), 0, st, \
+                         x, fn_w, T, n, R, chunks_per_range, part, scale, base);               \
     return hipGetLastError();                                                                  \
   }
   MHC_SP(1, 1) MHC_SP(1, 2) MHC_SP(1, 4)
