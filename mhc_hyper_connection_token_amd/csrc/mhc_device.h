@@ -115,12 +115,22 @@ __device__ __forceinline__ float col_sum(float v) {
 
 // iters rounds of: row pass C /= (row sum + eps), then column pass
 // C /= (column sum + eps).  The division is a hardware reciprocal (1 ulp) and a
-// multiply; zero entries stay zero.
+// multiply; zero entries stay zero.  Every sum runs over L lanes (padding
+// included), so each lane adds eps / L (exact: L is a power of two) to the
+// value it hands to the sum, in the same fused multiply-add that scales it;
+// the sum then carries the eps with no add of its own on the dependent chain.
+// The scaled entry itself is a plain rounded product.
 template <int L>
 __device__ __forceinline__ float sinkhorn_lanes(float c, int iters, float eps) {
+  const float el = eps * (1.0f / L);
+  float ce = c + el;
   for (int it = 0; it < iters; ++it) {
-    c *= __builtin_amdgcn_rcpf(row_sum<L>(c) + eps);
-    c *= __builtin_amdgcn_rcpf(col_sum<L>(c) + eps);
+    const float r = __builtin_amdgcn_rcpf(row_sum<L>(ce));
+    ce = fmaf(c, r, el);
+    c = __fmul_rn(c, r);
+    const float k = __builtin_amdgcn_rcpf(col_sum<L>(ce));
+    ce = fmaf(c, k, el);
+    c = __fmul_rn(c, k);
   }
   return c;
 }
