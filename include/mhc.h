@@ -34,8 +34,7 @@
  *    kernel).  Two calls enqueued on DIFFERENT streams of the same device must
  *    not run concurrently; calls on one stream are always safe.  The first
  *    call on a device that needs scratch allocates it, and a later call that
- *    needs more allocates a larger area (clearing its 256-byte header with
- *    hipMemsetAsync on that call's stream).  No scratch area is ever freed
+ *    needs more allocates a larger area.  No scratch area is ever freed
  *    before the process ends, so HIP graphs captured earlier stay valid.  A
  *    call that would have to grow the scratch while its stream is being
  *    captured returns MHC_ECAPTURE: make one call of the largest size before
@@ -98,7 +97,7 @@ int mhc_site_pre(const float* x, const float* fn_w, const float* scale, const fl
                  float* pre, float* post, float* comb, float* y, void* stream);
 
 /*
- * mhc_site_pre_scratch_bytes -- bytes of library scratch (header included) that
+ * mhc_site_pre_scratch_bytes -- bytes of library scratch that
  * mhc_site_pre needs for T tokens of this shape: the packed weight where the
  * large-batch kernel runs, else the split reduction's partial sums.  0 for
  * T < 1 or a shape the call rejects.  Host only: no HIP call, safe without a
@@ -113,10 +112,10 @@ size_t mhc_site_pre_scratch_bytes(int T, int streams, int hidden);
  * hipMalloc): the same arguments, checks, kernels and results, but the kernel
  * scratch is a fixed device array inside the library, 16 MiB on each GPU the
  * process uses, held until the process ends.  The call allocates, frees and
- * clears nothing.  A shape whose scratch (mhc_site_pre_scratch_bytes minus its
- * 256-byte header) exceeds 16 MiB returns MHC_EUNSUPPORTED before anything is
- * enqueued (large batches of short slabs can need more; the decode, verify,
- * prefill and wide sites need at most 10.7 MB).  Every call on a GPU shares that GPU's array
+ * clears nothing.  A shape whose scratch (mhc_site_pre_scratch_bytes) exceeds
+ * 16 MiB returns MHC_EUNSUPPORTED before anything is enqueued (large batches
+ * of short slabs can need more; the decode, verify, prefill and wide sites
+ * need at most 10.7 MB).  Every call on a GPU shares that GPU's array
  * (the last call's contents stay in it): two calls that overlap in time on one
  * GPU (different streams, or concurrent graph replays) race on it and must be
  * ordered by the caller.
@@ -296,10 +295,9 @@ int mhc_head_check(const float* x, const float* fn_w, const float* scale, const 
  * workspace needs (0 for an invalid shape; 1 <= max_tokens <= 8192).
  * mhc_workspace_init carves `mem` (device memory, 256-byte aligned, at least
  * that many bytes, owned by the caller and kept alive while the workspace is
- * used) into the regions below, fills *ws (host memory of the caller) and
- * clears the kernels' ticket with hipMemsetAsync on `stream`; it is not meant
- * to be captured.  Returns MHC_EINVAL / MHC_EALIGN / MHC_EUNSUPPORTED /
- * MHC_EHIP.
+ * used) into the regions below and fills *ws (host memory of the caller); it
+ * makes no HIP call and enqueues nothing.  Returns MHC_EINVAL / MHC_EALIGN /
+ * MHC_EUNSUPPORTED.
  *
  * The fields are read-only for the caller except that the current stream state
  * state[cur] may be written (e.g. the trunk's entry state) and read at any
@@ -326,14 +324,14 @@ typedef struct mhc_workspace {
   float* z;             /* [max_tokens][H] */
   signed char* q;       /* [max_tokens][H] */
   float* d;             /* [max_tokens][ceil(H/32)] */
-  void* scratch;        /* kernel scratch: ticket header + partials / packed weight */
-  size_t scratch_bytes; /* usable scratch after the header */
+  void* scratch;        /* kernel scratch: partials / packed weight */
+  size_t scratch_bytes; /* bytes of scratch */
 } mhc_workspace;
 
 size_t mhc_workspace_bytes(int max_tokens, int streams, int hidden);
 size_t mhc_workspace_struct_bytes(void); /* sizeof(mhc_workspace), for bindings */
 int mhc_workspace_init(mhc_workspace* ws, void* mem, size_t bytes, int max_tokens, int streams,
-                       int hidden, void* stream);
+                       int hidden);
 int mhc_ws_site_pre(mhc_workspace* ws, const float* fn_w, const float* scale, const float* base,
                     int T, int iters, float eps, void* stream);
 int mhc_ws_site_pre_zq8(mhc_workspace* ws, const float* fn_w, const float* scale,

@@ -84,7 +84,7 @@ def load_library() -> ctypes.CDLL:
     lib.mhc_workspace_bytes.restype = sz
     lib.mhc_workspace_struct_bytes.argtypes = []
     lib.mhc_workspace_struct_bytes.restype = sz
-    lib.mhc_workspace_init.argtypes = [wsp, vp, sz, i, i, i, vp]
+    lib.mhc_workspace_init.argtypes = [wsp, vp, sz, i, i, i]
     lib.mhc_workspace_init.restype = i
     lib.mhc_ws_site_pre.argtypes = [wsp, vp, vp, vp, i, i, fl, vp]
     lib.mhc_ws_site_pre.restype = i
@@ -471,7 +471,7 @@ class Workspace:
     ``pre``, ``post``, ``comb``, ``y``, ``z``, ``q``, ``d`` (max_tokens rows; a call
     with T tokens writes the first T)."""
 
-    def __init__(self, max_tokens: int, streams: int, hidden: int, device=None, stream=None):
+    def __init__(self, max_tokens: int, streams: int, hidden: int, device=None):
         import torch
         lib = load_library()
         nbytes = int(lib.mhc_workspace_bytes(max_tokens, streams, hidden))
@@ -484,7 +484,7 @@ class Workspace:
         off = (-base) % 256
         self._ws = _WsStruct()
         rc = lib.mhc_workspace_init(ctypes.byref(self._ws), base + off, nbytes, max_tokens,
-                                    streams, hidden, _stream_handle(stream))
+                                    streams, hidden)
         if rc != 0:
             raise MhcError("mhc_workspace_init", rc, _status_text(lib, rc))
         self.max_tokens, self.streams, self.hidden = max_tokens, streams, hidden

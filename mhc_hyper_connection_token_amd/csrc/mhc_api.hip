@@ -38,10 +38,8 @@ int check_shape(int T, int S, int H) {
   return MHC_OK;
 }
 
-// Library-owned scratch, one current buffer per device.  Its first
-// kScratchHeader bytes hold the decode kernels' ticket counter (cleared when the
-// buffer is allocated; the kernels leave it at zero); the rest is returned to
-// the caller (split-K partials, packed weight).
+// Library-owned scratch, one current buffer per device (split-K partials,
+// packed weight).
 //
 // A call that needs more than the current buffer allocates a larger one and
 // makes it current.  The smaller one is never freed: work already enqueued on
@@ -51,7 +49,6 @@ int check_shape(int T, int S, int H) {
 // hipMalloc, which HIP graph capture does not allow, so a call that would grow
 // the buffer while its stream is being captured returns MHC_ECAPTURE and
 // enqueues nothing; one call of the same size outside the capture sizes it.
-constexpr size_t kScratchHeader = 256;
 struct DeviceScratch {
   void* ptr = nullptr;
   size_t bytes = 0;
@@ -61,10 +58,9 @@ DeviceScratch g_scratch[64];
 
 struct Scratch {
   float* general = nullptr;
-  unsigned int* counter = nullptr;
 };
 
-// Bytes of the next buffer when `need` bytes (header included) are wanted and
+// Bytes of the next buffer when `need` bytes are wanted and
 // `have` are current: 1 MiB at least, then a quarter more than asked for.
 size_t scratch_grow_bytes(size_t need, size_t have) {
   if (need <= have) return have;
@@ -76,7 +72,7 @@ int get_scratch(size_t bytes, hipStream_t st, Scratch* out) {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MHC_EHIP;
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   DeviceScratch& s = g_scratch[dev];
-  const size_t need = bytes + kScratchHeader;
+  const size_t need = bytes;
   if (s.bytes < need) {
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(st, &cap) != hipSuccess) return MHC_EHIP;
@@ -84,14 +80,10 @@ int get_scratch(size_t bytes, hipStream_t st, Scratch* out) {
     const size_t want = scratch_grow_bytes(need, s.bytes);
     void* p = nullptr;
     if (hipMalloc(&p, want) != hipSuccess) return MHC_EHIP;
-    // the ticket starts at zero, ordered before this call's kernels
-    if (hipMemsetAsync(p, 0, kScratchHeader, st) != hipSuccess) return MHC_EHIP;
     s.ptr = p;  // the previous buffer stays allocated (see above)
     s.bytes = want;
   }
-  char* base = static_cast<char*>(s.ptr);
-  out->counter = reinterpret_cast<unsigned int*>(base);
-  out->general = reinterpret_cast<float*>(base + kScratchHeader);
+  out->general = static_cast<float*>(s.ptr);
   return MHC_OK;
 }
 
@@ -188,7 +180,7 @@ const char* mhc_status_string(int status) {
 
 size_t mhc_site_pre_scratch_bytes(int T, int streams, int hidden) {
   if (T < 1 || check_shape(T, streams, hidden) != MHC_OK) return 0;
-  return kScratchHeader + pre_scratch_bytes(T, streams, hidden);
+  return pre_scratch_bytes(T, streams, hidden);
 }
 
 int mhc_site_pre_check(const float* x, const float* fn_w, const float* scale, const float* base,
@@ -272,11 +264,13 @@ int site_pre_run(const float* x, const float* fn_w, const float* scale, const fl
     if ((rc = acquire_scratch(src, p.part_floats * sizeof(float), st, &sc))) return rc;
     float* part = sc.general;
     hipError_t e;
-    if (zq && sc.counter && mhc::decode_zq8_supported(T, S, H, p.G)) {
-      // one decode token with the epilogue: one launch; the block that draws
-      // the last ticket finishes
-      e = mhc::launch_decode_zq8(x, fn_w, scale, base, T, S, H, iters, eps, p.G, p.cpr, part,
-                                 sc.counter, pre, post, comb, y, *zq, st);
+    if (zq && mhc::finish_zq8_supported(T, S, H)) {
+      // one decode token with the epilogue: the partials, then two blocks that
+      // finish (one runs the Sinkhorn, the other the collapse and epilogue)
+      e = mhc::launch_small_partials(x, fn_w, T, S, H, p.G, p.cpr, part, st, scale, base);
+      if (e == hipSuccess)
+        e = mhc::launch_finish_zq8(x, part, p.G, S, H, scale, base, iters, eps, pre, post, comb,
+                                   y, *zq, st);
       zq_done = true;
     } else {
       // S <= 4 below the fused threshold: the vector-ALU partials
@@ -681,8 +675,7 @@ int mhc_head(const float* x, const float* fn_w, const float* scale, const float*
 
 // ---------------------------------------------------------------- workspace
 // Caller memory carved into 256-byte aligned regions, in this order: the kernel
-// scratch (ticket header + the largest partials / packed weight of any
-// T <= max_tokens), the two stream states, pre, post, comb, y, z, q, d.
+// scratch (the largest partials / packed weight of any T <= max_tokens), the two stream states, pre, post, comb, y, z, q, d.
 namespace {
 constexpr size_t kWsAlign = 256;
 size_t ws_round(size_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; }
@@ -700,7 +693,7 @@ bool ws_layout(int max_tokens, int S, int H, WsLayout* L) {
     if (b > general) general = b;
   }
   const size_t T = max_tokens;
-  const size_t sizes[10] = {kScratchHeader + general, T * S * H * 4, T * S * H * 4, T * S * 4,
+  const size_t sizes[10] = {general, T * S * H * 4, T * S * H * 4, T * S * 4,
                             T * S * 4, T * S * S * 4, T * H * 4, T * H * 4, T * H,
                             T * ((H + 31) / 32) * 4};
   size_t o = 0;
@@ -720,9 +713,7 @@ int ws_ok(const mhc_workspace* ws, int T) {
 }
 
 ScratchSource ws_scratch(const mhc_workspace* ws, Scratch* holder) {
-  char* b = static_cast<char*>(ws->scratch);
-  holder->counter = reinterpret_cast<unsigned int*>(b);
-  holder->general = reinterpret_cast<float*>(b + kScratchHeader);
+  holder->general = static_cast<float*>(ws->scratch);
   ScratchSource src;
   src.fixed = holder;
   src.bytes = ws->scratch_bytes;
@@ -740,7 +731,7 @@ size_t mhc_workspace_bytes(int max_tokens, int streams, int hidden) {
 size_t mhc_workspace_struct_bytes(void) { return sizeof(mhc_workspace); }
 
 int mhc_workspace_init(mhc_workspace* ws, void* mem, size_t bytes, int max_tokens, int streams,
-                       int hidden, void* stream) {
+                       int hidden) {
   if (!ws || !mem) return MHC_EINVAL;
   WsLayout L;
   if (!ws_layout(max_tokens, streams, hidden, &L)) {
@@ -765,10 +756,6 @@ int mhc_workspace_init(mhc_workspace* ws, void* mem, size_t bytes, int max_token
   ws->z = reinterpret_cast<float*>(b + L.off[7]);
   ws->q = reinterpret_cast<signed char*>(b + L.off[8]);
   ws->d = reinterpret_cast<float*>(b + L.off[9]);
-  // the decode ticket starts at zero; the kernels leave it there
-  if (hipMemsetAsync(ws->scratch, 0, kScratchHeader, static_cast<hipStream_t>(stream)) !=
-      hipSuccess)
-    return MHC_EHIP;
   return MHC_OK;
 }
 
@@ -866,11 +853,8 @@ int mhc_site_pre_static(const float* x, const float* fn_w, const float* scale, c
   if (need > kStaticScratchBytes) return MHC_EUNSUPPORTED;
   void* p = nullptr;
   if ((rc = static_scratch(&p))) return rc;
-  // the pre chain without the epilogue uses no ticket, so the whole array is
-  // the general region
   Scratch holder;
   holder.general = static_cast<float*>(p);
-  holder.counter = nullptr;
   ScratchSource src;
   src.fixed = &holder;
   src.bytes = kStaticScratchBytes;

@@ -77,6 +77,124 @@ __global__ __launch_bounds__(256) void finish_kernel(
   }
 }
 
+// One decode token (T = 1, S <= 4) with the branch-input epilogue (hc_fused_gate.rs
+// page, the v4z timing block: RMS norm of y with nw, q8 codes and block scales).
+// Two blocks that each add the partials in the fixed order above:
+//   block 0: comb (gates and Sinkhorn) on wave 0, pre and post on wave 3;
+//   block 1: the collapse of every hidden quad (quads tid + 256k, y kept in
+//            registers), then the epilogue exactly as the standalone epilogue
+//            kernel computes it (the same per-thread sums, the same block tree),
+//            so that z, q and d equal the two-launch result bit for bit.
+// The epilogue block never waits for the Sinkhorn.  Block 1 requests its x
+// and nw quads right behind the partials (block 0 requests the same offsets
+// out of range, so that both blocks run the same wait sequence).
+template <int KQ>
+__global__ __launch_bounds__(256) void finish_zq8_kernel(
+    const float* __restrict__ x, const float* __restrict__ part, int G, int S, int H,
+    const float* __restrict__ scale, const float* __restrict__ base, int iters, float eps,
+    float* __restrict__ pre, float* __restrict__ post, float* __restrict__ comb,
+    float* __restrict__ y, Zq8Out zq) {
+  const int R = (2 + S) * S;
+  const int RP = R + 1;
+  const int n = S * H;
+  const int HQ = H >> 2;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  __shared__ float red[256];
+  __shared__ float m_raw[32];
+  __shared__ float params[3 + 24];
+  __shared__ float pre_lds[8];
+  stage_site_params(scale, base, R, params);
+  const bool gates = blockIdx.x == 0;  // block-uniform
+
+  const __amdgpu_buffer_rsrc_t xrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(x), (short)0, n * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(zq.nw), (short)0, H * 4, 0x00020000);
+  float4 xq[KQ][4], wq[KQ];
+  auto ld = [](__amdgpu_buffer_rsrc_t rs, int off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                       __uint_as_float(v[3]));
+  };
+  auto request = [&]() {
+#pragma unroll
+    for (int k = 0; k < KQ; ++k) {
+      const int q = tid + 256 * k;
+      // streams past S, quads past H / 4 and block 0's requests fall past the
+      // end of their buffer and read zero
+      int off = (!gates && q < HQ) ? 16 * q : 0x7FFFFFF0;
+      asm volatile("" : "+v"(off));  // a plain offset, not a branch per load
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xq[k][c] = ld(xrs, off + c * H * 4);
+      wq[k] = ld(wrs, off);
+    }
+  };
+  reduce_token_partials<false, 16>(part, G, 1, 0, RP, red, m_raw, request);
+
+  if (gates) {
+    if (wave == 0)
+      gates_comb<4>(m_raw, 0, 1, S, n, params, iters, eps, true, comb);
+    else if (wave == 3)
+      gates_pre_post<4>(m_raw, 0, 1, S, n, params, eps, true, pre, post, pre_lds);
+    return;
+  }
+
+  float pc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) pc[c] = c < S ? pre_gate(m_raw, c, R, n, eps, params) : 0.f;
+  float4 yk[KQ];
+  float ss = 0.f;
+  float4* y4 = reinterpret_cast<float4*>(y);
+#pragma unroll
+  for (int k = 0; k < KQ; ++k) {
+    const int q = tid + 256 * k;
+    yk[k] = q < HQ ? collapse4<4>(pc, xq[k], S) : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (q < HQ) y4[q] = yk[k];
+    ss = sq4(yk[k], ss);
+  }
+  red[tid] = ss;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
+    __syncthreads();
+  }
+  const float r = zq8_rinv(red[0], H, zq.norm_eps);
+  float4* zt = reinterpret_cast<float4*>(zq.z);
+  char4* qt = reinterpret_cast<char4*>(zq.q);
+#pragma unroll
+  for (int k = 0; k < KQ; ++k) {
+    const int q = tid + 256 * k;
+    const bool in = q < HQ;  // HQ % 8 == 0: a 32-entry block is all in or all out
+    const float4 o = zq8_norm(yk[k], r, wq[k]);
+    float db;
+    const char4 cq = zq8_codes(o, &db);
+    if (in) {
+      zt[q] = o;
+      qt[q] = cq;
+      if ((tid & 7) == 0) zq.d[q >> 3] = db;
+    }
+  }
+}
+
+bool finish_zq8_supported(int T, int S, int H) {
+  return T == 1 && S >= 1 && S <= 4 && H % 32 == 0 && H / 4 <= 8 * 256;
+}
+
+hipError_t launch_finish_zq8(const float* x, const float* part, int G, int S, int H,
+                             const float* scale, const float* base, int iters, float eps,
+                             float* pre, float* post, float* comb, float* y, const Zq8Out& zq,
+                             hipStream_t st) {
+  if (!finish_zq8_supported(1, S, H)) return hipErrorInvalidValue;
+  if (H / 4 <= 4 * 256)
+    hipLaunchKernelGGL((finish_zq8_kernel<4>), dim3(2), dim3(256), 0, st, x, part, G, S, H, scale,
+                       base, iters, eps, pre, post, comb, y, zq);
+  else
+    hipLaunchKernelGGL((finish_zq8_kernel<8>), dim3(2), dim3(256), 0, st, x, part, G, S, H, scale,
+                       base, iters, eps, pre, post, comb, y, zq);
+  return hipGetLastError();
+}
+
 hipError_t launch_finish(const float* x, const float* part, int G, int T, int S, int H,
                          const float* scale, const float* base, int iters, float eps,
                          float* pre, float* post, float* comb, float* y, hipStream_t st) {

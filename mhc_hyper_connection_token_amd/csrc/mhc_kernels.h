@@ -71,15 +71,12 @@ hipError_t launch_fused_head(const float* x, const float* fn_h, const float* sca
                              const float* base_h, int T, int S, int H, float eps, float* gates,
                              float* y, float* wpack, hipStream_t st);
 
-// Single-launch pre chain and branch-input epilogue of one token (S <= 4,
-// H % 32 == 0; decode_zq8_supported): split-K partials into `part` (same G /
-// chunks_per_range as the two-kernel path), the last block (ticket on
-// `counter`, which must be zero on entry and is zero again on exit) finishes.
-bool decode_zq8_supported(int T, int S, int H, int G);
-hipError_t launch_decode_zq8(const float* x, const float* fn_w, const float* scale,
-                             const float* base, int T, int S, int H, int iters, float eps, int G,
-                             int chunks_per_range, float* part, unsigned int* counter, float* pre,
-                             float* post, float* comb, float* y, const Zq8Out& zq,
+// One decode token's finish with the branch-input epilogue (T = 1, S <= 4,
+// H % 32 == 0, H <= 8192): the partials as launch_finish takes them.
+bool finish_zq8_supported(int T, int S, int H);
+hipError_t launch_finish_zq8(const float* x, const float* part, int G, int S, int H,
+                             const float* scale, const float* base, int iters, float eps,
+                             float* pre, float* post, float* comb, float* y, const Zq8Out& zq,
                              hipStream_t st);
 
 // Branch-input epilogue: z = RMS-norm(y) * nw and its q8 codes / block scales,

@@ -2,6 +2,8 @@
 // partials, finish and single-launch decode kernels so that all of them add
 // the same numbers in the same order.
 #pragma once
+#include <type_traits>
+
 #include "mhc_device.h"
 
 namespace mhc {
@@ -476,30 +478,66 @@ __device__ __forceinline__ void small_partials_groups(const float* __restrict__ 
 
 // Fixed-order sum of the G partials of token t into m_out[0..R] (256 threads):
 // thread (r, q), q < Q = 256 / (R+1), adds g = q, q + Q, q + 2Q, ... in that
-// order (eight independent loads in flight per batch); then thread r adds the Q
+// order (BATCH independent loads in flight per batch); then thread r adds the Q
 // sums in q order.  The order depends only on G and R, not on T.  Ends with a
-// block barrier; m_out is in LDS.
-template <bool COHERENT = false, int BATCH = 8>
+// block barrier; m_out is in LDS.  issue() runs in every thread right after
+// the first batch of loads is requested: loads it requests complete after the
+// partials (a wave's loads complete in order), so the reduction does not wait
+// for them.
+struct NoIssue {
+  __device__ __forceinline__ void operator()() const {}
+};
+template <bool COHERENT = false, int BATCH = 8, class Issue = NoIssue>
 __device__ __forceinline__ void reduce_token_partials(const float* __restrict__ part, int G, int T,
                                                       int t, int RP, float* red256,
-                                                      float* m_out) {
+                                                      float* m_out, Issue issue = Issue()) {
   const int Q = 256 / RP;
   {
     const int r = threadIdx.x % RP, q = threadIdx.x / RP;
+    const float* p = part + (size_t)t * RP + r;
+    const size_t gstride = (size_t)T * RP;
     float s = 0.f;
-    if (q < Q) {
-      const float* p = part + (size_t)t * RP + r;
-      const size_t gstride = (size_t)T * RP;
-      for (int g0 = q; g0 < G; g0 += BATCH * Q) {
-        float v[BATCH];
+    if constexpr (std::is_same_v<Issue, NoIssue>) {
+      if (q < Q) {
+        for (int g0 = q; g0 < G; g0 += BATCH * Q) {
+          float v[BATCH];
+#pragma unroll
+          for (int u = 0; u < BATCH; ++u) {
+            const int g = g0 + u * Q;
+            v[u] = load_partial<COHERENT>(p + (size_t)(g < G ? g : q) * gstride);
+          }
+#pragma unroll
+          for (int u = 0; u < BATCH; ++u)
+            if (g0 + u * Q < G) s += v[u];
+        }
+      }
+    } else {
+      // the same sums, with the first batch peeled so that issue() follows it
+      float v[BATCH];
+      if (q < Q) {
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
-          const int g = g0 + u * Q;
+          const int g = q + u * Q;
           v[u] = load_partial<COHERENT>(p + (size_t)(g < G ? g : q) * gstride);
         }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      issue();
+      __builtin_amdgcn_sched_barrier(0);
+      if (q < Q) {
 #pragma unroll
         for (int u = 0; u < BATCH; ++u)
-          if (g0 + u * Q < G) s += v[u];
+          if (q + u * Q < G) s += v[u];
+        for (int g0 = q + BATCH * Q; g0 < G; g0 += BATCH * Q) {
+#pragma unroll
+          for (int u = 0; u < BATCH; ++u) {
+            const int g = g0 + u * Q;
+            v[u] = load_partial<COHERENT>(p + (size_t)(g < G ? g : q) * gstride);
+          }
+#pragma unroll
+          for (int u = 0; u < BATCH; ++u)
+            if (g0 + u * Q < G) s += v[u];
+        }
       }
     }
     red256[threadIdx.x] = s;

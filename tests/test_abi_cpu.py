@@ -169,8 +169,8 @@ def test_workspace_bytes_cover_every_region(lib):
         regions = (2 * T * S * H * 4 + 2 * T * S * 4 + T * S * S * 4 + 2 * T * H * 4 + T * H
                    + T * ((H + 31) // 32) * 4)
         assert b % 256 == 0
-        # the regions plus the ticket header and at least one token's partials
-        assert b >= regions + 256 + (R + 1) * 4
+        # the regions plus at least one token's partials
+        assert b >= regions + (R + 1) * 4
         assert mhc.workspace_bytes(T + 1, S, H) >= b if T < 8192 else True
 
 
@@ -187,14 +187,24 @@ def test_workspace_struct_matches_binding(lib):
 def test_workspace_init_refuses_before_any_gpu_work(lib):
     ws = mhc._WsStruct()
     need = mhc.workspace_bytes(4, 4, 4096)
-    assert lib.mhc_workspace_init(None, 1 << 30, need, 4, 4, 4096, None) == EINVAL
-    assert lib.mhc_workspace_init(ctypes.byref(ws), None, need, 4, 4, 4096, None) == EINVAL
-    assert lib.mhc_workspace_init(ctypes.byref(ws), (1 << 30) + 16, need, 4, 4, 4096,
-                                  None) == EALIGN
-    assert lib.mhc_workspace_init(ctypes.byref(ws), 1 << 30, need - 256, 4, 4, 4096,
-                                  None) == EINVAL
-    assert lib.mhc_workspace_init(ctypes.byref(ws), 1 << 30, need, 4, 9, 4096, None) == EUNSUP
-    assert lib.mhc_workspace_init(ctypes.byref(ws), 1 << 30, need, 0, 4, 4096, None) == EINVAL
+    assert lib.mhc_workspace_init(None, 1 << 30, need, 4, 4, 4096) == EINVAL
+    assert lib.mhc_workspace_init(ctypes.byref(ws), None, need, 4, 4, 4096) == EINVAL
+    assert lib.mhc_workspace_init(ctypes.byref(ws), (1 << 30) + 16, need, 4, 4, 4096) == EALIGN
+    assert lib.mhc_workspace_init(ctypes.byref(ws), 1 << 30, need - 256, 4, 4, 4096) == EINVAL
+    assert lib.mhc_workspace_init(ctypes.byref(ws), 1 << 30, need, 4, 9, 4096) == EUNSUP
+    assert lib.mhc_workspace_init(ctypes.byref(ws), 1 << 30, need, 0, 4, 4096) == EINVAL
+
+
+def test_workspace_init_makes_no_hip_call(lib):
+    """Initialisation only carves the caller's memory: at a fake, aligned device
+    address it succeeds without a GPU and lays the regions out in order."""
+    ws = mhc._WsStruct()
+    base = 1 << 30
+    need = mhc.workspace_bytes(4, 4, 4096)
+    assert lib.mhc_workspace_init(ctypes.byref(ws), base, need, 4, 4, 4096) == OK
+    assert ws.scratch == base and ws.cur == 0
+    assert ws.state[0] > ws.scratch and ws.state[1] > ws.state[0]
+    assert ws.d + 4 * 128 * 4 <= base + need
 
 
 def test_ws_calls_refuse_before_any_gpu_work(lib):
@@ -310,10 +320,10 @@ def test_packed_weight_calls_refuse_before_any_gpu_work(lib):
 
 
 def test_pre_scratch_bytes_follow_the_kernel_choice(lib):
-    """The library scratch a pre call needs: a 256-byte header plus the packed
-    weight where the token-tiled kernel runs (S <= 4, T >= 256), else the split
-    reduction's partials, G K-ranges x T tokens x (R + 1) floats."""
-    hdr = 256
+    """The library scratch a pre call needs: the packed weight where the
+    token-tiled kernel runs (S <= 4, T >= 256), else the split reduction's
+    partials, G K-ranges x T tokens x (R + 1) floats."""
+    hdr = 0
     packed = mhc.packed_weight_bytes(4, 4096)
     assert packed == 8 * 4 * 8 * 6 * 64 * 16  # 8 waves x 32 chunks x 6 row groups x 1 KiB
     assert mhc.site_pre_scratch_bytes(4096, 4, 4096) == hdr + packed

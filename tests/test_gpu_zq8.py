@@ -80,9 +80,9 @@ def test_zq8_prefill_every_token(mhc):
     _check(mhc, make_site(c), c.iters, c.eps, "prefill")
 
 
-# Paths: one token with S <= 4 runs the epilogue in the single-launch decode
-# kernel, T >= 256 with an on-chip slab in the fused kernel's tail, everything
-# else as a launch of its own after the split path.
+# Paths: one token with S <= 4 runs the epilogue in its two-block finish,
+# T >= 256 with an on-chip slab in the fused kernel's tail, everything else as
+# a launch of its own after the split path.
 @pytest.mark.parametrize("T,S,H", [(1, 1, 32), (1, 4, 8192), (2, 4, 4096), (2, 3, 4608),
                                    (2, 4, 8192), (2, 8, 7168), (3, 2, 64), (17, 4, 1024),
                                    (128, 2, 1056), (130, 4, 4096), (131, 1, 8192),
@@ -104,3 +104,23 @@ def test_zq8_zero_input_gives_zero_codes(mhc):
     torch.cuda.synchronize()
     y, z, q, dd = [o.cpu().numpy() for o in out[3:]]
     assert np.all(y == 0) and np.all(z == 0) and np.all(q == 0) and np.all(dd == 0)
+
+
+def test_zq8_decode_token_matches_its_row_in_a_batch(mhc):
+    """One decode token (its own two-block finish with the epilogue) against the
+    same token as row 0 of a two-token batch (the split path, then the
+    standalone epilogue launch): the same partials and the same sums, so every
+    output is equal bit for bit."""
+    c = CONFIGS["decode"]
+    d = make_site(c)
+    d2 = make_random_shape(2, c.S, c.H, seed=77)
+    x2 = np.concatenate([d["x"], d2["x"][1:]], axis=0)
+    nw = make_norm_weight(c.H)
+    print("[case] zq8 decode token vs batched row", flush=True)
+    one = mhc.site_pre_zq8(_dev(d["x"]), _dev(d["fn_w"]), _dev(d["scale"]), _dev(d["base"]),
+                           _dev(nw), c.iters, c.eps, NORM_EPS)
+    two = mhc.site_pre_zq8(_dev(x2), _dev(d["fn_w"]), _dev(d["scale"]), _dev(d["base"]),
+                           _dev(nw), c.iters, c.eps, NORM_EPS)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("pre", "post", "comb", "y", "z", "q", "d"), one, two):
+        assert np.array_equal(a.cpu().numpy()[0], b.cpu().numpy()[0]), name
