@@ -233,8 +233,8 @@ int mhc_site_post_check(const float* x, const float* f, const float* post, const
 namespace {
 
 // The pre chain for checked arguments.  With zq, the branch-input epilogue runs
-// in the tail of the fused and single-launch decode kernels where they support
-// it, otherwise as its own launch after the chain.
+// in the tail of the fused kernels and in the one-token finish where they
+// support it, otherwise as its own launch after the chain.
 int site_pre_run(const float* x, const float* fn_w, const float* scale, const float* base, int T,
                  int S, int H, int iters, float eps, float* pre, float* post, float* comb,
                  float* y, const mhc::Zq8Out* zq, hipStream_t st,

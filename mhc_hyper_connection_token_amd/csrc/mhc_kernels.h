@@ -19,8 +19,8 @@ struct Zq8Out {
 hipError_t launch_partials(const float* x, const float* fn_w, int T, int n, int R, int ntt,
                            int G, int chunks_per_range, float* part, hipStream_t st);
 
-// Vector-ALU split-K partials (S <= 4, any T in groups of 16 tokens), per token
-// in the order the single-launch decode kernel uses; same part layout.  With
+// Vector-ALU split-K partials (S <= 4, any T in groups of 4 tokens, or one
+// token), every token's sums in one fixed order; same part layout.  With
 // scale / base given, one block also reads the site parameters first thing, so
 // that the finish kernel finds them in the memory-side cache.
 int small_rows_per_thread(int S);

@@ -71,9 +71,8 @@ static hipError_t launch_partials_t(const float* x, const float* fn_w, int T, in
   return hipGetLastError();
 }
 
-// Vector-ALU partials (S <= 4), one token at a time in the same order as the
-// single-launch decode kernel, so a token's result does not depend on the
-// batch it is in.  Grid: (G K-ranges, Y); block (g, y) takes the groups of
+// Vector-ALU partials (S <= 4), every token's sums in the same order whatever
+// the group size, so a token's result does not depend on the batch it is in.  Grid: (G K-ranges, Y); block (g, y) takes the groups of
 // kSmallGroup tokens y, y + Y, ..., with the weight quads of its K-range held
 // in registers and the next group's x requested while the current one is
 // reduced.  QL = column quads per lane (a K-range of at most 128*QL floats).

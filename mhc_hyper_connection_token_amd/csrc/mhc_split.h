@@ -1,6 +1,6 @@
 // mhc_split.h -- device routines of the split-K pre path, shared by the
-// partials, finish and single-launch decode kernels so that all of them add
-// the same numbers in the same order.
+// partials and finish kernels so that all of them add the same numbers in the
+// same order.
 #pragma once
 #include <type_traits>
 

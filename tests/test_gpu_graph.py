@@ -1,8 +1,9 @@
 """HIP graph capture of whole sites: every replay equals the eager result bit for bit.
 
-Covers the pre schedules (single-launch decode, split partials + finish,
-packed-weight fused tiles, and at the prefill chunk the persistent tiles that
-request half of each next slab into LDS) and the post kernel.  Every replay is also compared
+Covers the pre schedules (split partials + finish, the one-token finish with
+the branch-input epilogue, packed-weight fused tiles, and at the prefill chunk
+the persistent tiles that request half of each next slab into LDS) and the post
+kernel.  Every replay is also compared
 with the fp64 oracle on every token.  Between replays the program
 runs its own eager work (a different site through the same library scratch)
 and synchronises, so a replay that depended on state left by the capture, or
@@ -13,7 +14,7 @@ import pytest
 
 import oracle
 from mhc_inputs import make_random_shape
-from parity import check_site_with_oracle
+from parity import assert_streams_close, check_site_with_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -83,6 +84,51 @@ def test_graph_replays_match_eager(mhc, T, S, H):
         check_site_with_oracle(host["x"], host, [t.cpu().numpy() for t in out_pre], iters, eps,
                                f"graph T{T} S{S} H{H} replay {rep}",
                                x_out=out_x.cpu().numpy(), oracle_pre=o_ref)
+
+
+def test_graph_replays_match_eager_with_the_epilogue(mhc):
+    """One decode token with the branch-input epilogue (partials, then the
+    two-block finish) captured in a graph: every replay equals the eager call bit
+    for bit, and its pre outputs and z match the fp64 oracle."""
+    from mhc_inputs import make_norm_weight
+    iters, eps, norm_eps = 20, 1e-6, 1e-5
+    T, S, H = 1, 4, 4096
+    print("[case] graph T=1 with the epilogue", flush=True)
+    d = {k: torch.from_numpy(v).cuda() for k, v in make_random_shape(T, S, H, 21).items()}
+    other = {k: torch.from_numpy(v).cuda() for k, v in make_random_shape(T, S, H, 22).items()}
+    nw = torch.from_numpy(make_norm_weight(H)).cuda()
+    out = mhc.site_pre_zq8(d["x"], d["fn_w"], d["scale"], d["base"], nw, iters, eps, norm_eps)
+    o2 = mhc.site_pre_zq8(other["x"], other["fn_w"], other["scale"], other["base"], nw, iters,
+                          eps, norm_eps)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        mhc.site_pre_zq8(d["x"], d["fn_w"], d["scale"], d["base"], nw, iters, eps, norm_eps,
+                         out=out)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in out]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        mhc.site_pre_zq8(d["x"], d["fn_w"], d["scale"], d["base"], nw, iters, eps, norm_eps,
+                         out=out)
+    torch.cuda.synchronize()
+    host = {k: v.cpu().numpy() for k, v in d.items()}
+    for rep in range(3):
+        for t in out:
+            t.fill_(0)
+        with torch.cuda.stream(s):
+            mhc.site_pre_zq8(other["x"], other["fn_w"], other["scale"], other["base"], nw, iters,
+                             eps, norm_eps, out=o2)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("pre", "post", "comb", "y", "z", "q", "d"), out, ref):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager result"
+        got = [t.cpu().numpy() for t in out]
+        check_site_with_oracle(host["x"], host, got[:4], iters, eps,
+                               f"graph epilogue replay {rep}")
+        assert_streams_close(got[4], oracle.rmsnorm(got[3], nw.cpu().numpy(), norm_eps),
+                             f"graph epilogue replay {rep} z")
 
 
 def test_graph_survives_scratch_growth_and_capture_refuses_growth(mhc):

@@ -68,8 +68,8 @@ def _walk_fused(mhc, x0, sites, nw):
 
 
 # T >= 256, S <= 4: the fused pre kernel with the post prologue; every other
-# shape: the post kernel, then the pre chain (small-batch split, single-launch
-# decode kernel with the epilogue, MFMA split for S > 4).
+# shape: the post kernel, then the pre chain (small-batch split, the one-token
+# finish with the epilogue, MFMA split for S > 4).
 @pytest.mark.parametrize("T,S,H,zq", [(256, 4, 4096, False), (300, 4, 1024, False),
                                       (260, 2, 1056, True), (256, 4, 4096, True),
                                       (1, 4, 4096, False), (2, 4, 4096, True),

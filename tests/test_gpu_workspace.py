@@ -185,8 +185,8 @@ def test_ws_graph_replays_equal_eager_walk(mhc, T, S, H, use_zq8):
 
 
 def test_two_workspaces_on_two_streams(mhc):
-    """Each workspace has its own scratch and ticket, so two walks may run on two
-    streams at once."""
+    """Each workspace has its own scratch, so two walks may run on two streams at
+    once."""
     T, S, H = 1, 4, 4096
     print("[case] two workspaces, two streams", flush=True)
     xa0, sa = _sites(T, S, H, 4, seed=71)
