@@ -203,7 +203,11 @@ __device__ __forceinline__ void gates_pre_post(const float* mraw, int ldm, int n
                                                int n, const float* params, float eps,
                                                bool write_out, float* __restrict__ pre,
                                                float* __restrict__ post, float* pre_lds) {
-  const int lane = threadIdx.x & (kWave - 1);
+  // The lane index through an opaque copy: in a kernel that loops over tiles,
+  // the per-lane output offsets derived from it would otherwise be hoisted out
+  // of the loop and held (or spilled) across it.
+  int lane = threadIdx.x & (kWave - 1);
+  asm volatile("" : "+v"(lane));
   const int R = (2 + S) * S;
   const float s_post = params[1];
   const float* base = params + 3;
@@ -235,7 +239,8 @@ template <int L>
 __device__ __forceinline__ void gates_comb(const float* mraw, int ldm, int ntok, int S, int n,
                                            const float* params, int iters, float eps,
                                            bool write_out, float* __restrict__ comb) {
-  const int lane = threadIdx.x & (kWave - 1);
+  int lane = threadIdx.x & (kWave - 1);  // opaque, as in gates_pre_post
+  asm volatile("" : "+v"(lane));
   const int R = (2 + S) * S;
   const float s_comb = params[2];
   const float* base = params + 3;

@@ -94,6 +94,9 @@ def test_config_parity_full_size_every_token(mhc, name):
     # mid-size batches on the solo K-split (S <= 4, T < 256)
     (127, 4, 4096, 20), (128, 4, 4096, 20), (131, 3, 1028, 20), (129, 4, 68, 20),
     (200, 1, 8192, 20), (255, 2, 4, 5),
+    # one token (one-token partial groups): row counts per thread 1, 2, 2, 4 and
+    # column quads per lane 1, 2 and 4
+    (1, 1, 260, 20), (1, 2, 36, 20), (1, 3, 1028, 20), (1, 4, 8192, 20), (1, 4, 16000, 20),
     # batches large enough for the token-tiled fused kernel (S <= 4, T >= 256)
     (256, 4, 4096, 20), (259, 3, 1028, 20), (300, 2, 4, 5), (261, 4, 2052, 1),
     (257, 4, 68, 20), (320, 1, 8192, 20),

@@ -83,7 +83,7 @@ def test_zq8_prefill_every_token(mhc):
 # Paths: one token with S <= 4 runs the epilogue in its two-block finish,
 # T >= 256 with an on-chip slab in the fused kernel's tail, everything else as
 # a launch of its own after the split path.
-@pytest.mark.parametrize("T,S,H", [(1, 1, 32), (1, 4, 8192), (2, 4, 4096), (2, 3, 4608),
+@pytest.mark.parametrize("T,S,H", [(1, 1, 32), (1, 2, 64), (1, 3, 4608), (1, 4, 8192), (2, 4, 4096), (2, 3, 4608),
                                    (2, 4, 8192), (2, 8, 7168), (3, 2, 64), (17, 4, 1024),
                                    (128, 2, 1056), (130, 4, 4096), (131, 1, 8192),
                                    (256, 2, 1056), (258, 4, 4096), (259, 1, 8192),
