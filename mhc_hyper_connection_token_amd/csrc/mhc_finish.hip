@@ -112,8 +112,8 @@ __global__ __launch_bounds__(256) void finish_zq8_kernel(
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(zq.nw), (short)0, H * 4, 0x00020000);
   float4 xq[KQ][4], wq[KQ];
-  auto ld = [](__amdgpu_buffer_rsrc_t rs, int off) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+  auto ld = [](__amdgpu_buffer_rsrc_t rs, unsigned off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
     return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
                        __uint_as_float(v[3]));
   };
@@ -122,11 +122,11 @@ __global__ __launch_bounds__(256) void finish_zq8_kernel(
     for (int k = 0; k < KQ; ++k) {
       const int q = tid + 256 * k;
       // streams past S, quads past H / 4 and block 0's requests fall past the
-      // end of their buffer and read zero
-      int off = (!gates && q < HQ) ? 16 * q : 0x7FFFFFF0;
+      // end of their buffer and read zero (offsets are unsigned to the unit)
+      unsigned off = (!gates && q < HQ) ? 16u * q : 0x7FFFFFF0u;
       asm volatile("" : "+v"(off));  // a plain offset, not a branch per load
 #pragma unroll
-      for (int c = 0; c < 4; ++c) xq[k][c] = ld(xrs, off + c * H * 4);
+      for (int c = 0; c < 4; ++c) xq[k][c] = ld(xrs, off + (unsigned)c * (unsigned)H * 4u);
       wq[k] = ld(wrs, off);
     }
   };
