@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void finish_kernel(
   if (early && qa < q1) load_quads(qa);
 
   // 1. fixed-order reduction of the G partials
-  reduce_token_partials<false, 16>(part, G, T, t, RP, red, m_raw);
+  reduce_token_partials<16>(part, G, T, t, RP, red, m_raw);
 
   // 2. block 0: comb (gates and Sinkhorn) on wave 0, pre and post on wave 3
   if (hb == 0) {
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void finish_zq8_kernel(
       wq[k] = ld(wrs, off);
     }
   };
-  reduce_token_partials<false, 16>(part, G, 1, 0, RP, red, m_raw, request);
+  reduce_token_partials<16>(part, G, 1, 0, RP, red, m_raw, request);
 
   if (gates) {
     if (wave == 0)

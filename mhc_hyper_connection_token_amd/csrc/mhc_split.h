@@ -8,6 +8,18 @@
 
 namespace mhc {
 
+// Values each lane of a wave hands to the cross-wave sum, and the number of
+// slices that sum is staged in (the caller's `red` holds 4 * block_slice * 64
+// floats).
+template <int NRT, int NTT>
+constexpr int block_vals() { return NRT * NTT * 4 + NTT; }
+template <int NRT, int NTT>
+constexpr int block_passes() { return block_vals<NRT, NTT>() > 48 ? 2 : 1; }
+template <int NRT, int NTT>
+constexpr int block_slice() {
+  return (block_vals<NRT, NTT>() + block_passes<NRT, NTT>() - 1) / block_passes<NRT, NTT>();
+}
+
 // Per-block split-K partials (hyper.rs page, module doc: arithmetic contract,
 // first two lines): for tokens [tok0, tok0 + 16*NTT) and the 16-float K chunks
 // [c_beg, c_end) of the slab, the partial dots with the R weight rows and the
@@ -22,34 +34,6 @@ namespace mhc {
 // (16 tokens per tile).  Each lane loads 16 bytes of one weight row and 16
 // bytes of one token slab per chunk; the four floats feed four MFMAs whose
 // k-index is whatever the lanes hold (A and B agree by construction).
-// Plain store, or (COHERENT) an agent-scope relaxed atomic store that is
-// written through to the device-coherent level, for partials that another
-// block reads in the same launch.
-template <bool COHERENT>
-__device__ __forceinline__ void store_partial(float* p, float v) {
-  if (COHERENT)
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else
-    *p = v;
-}
-template <bool COHERENT>
-__device__ __forceinline__ float load_partial(const float* p) {
-  if (COHERENT) return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return *p;
-}
-
-// Values each lane of a wave hands to the cross-wave sum, and the number of
-// slices that sum is staged in (the caller's `red` holds 4 * block_slice * 64
-// floats).
-template <int NRT, int NTT>
-constexpr int block_vals() { return NRT * NTT * 4 + NTT; }
-template <int NRT, int NTT>
-constexpr int block_passes() { return block_vals<NRT, NTT>() > 48 ? 2 : 1; }
-template <int NRT, int NTT>
-constexpr int block_slice() {
-  return (block_vals<NRT, NTT>() + block_passes<NRT, NTT>() - 1) / block_passes<NRT, NTT>();
-}
-
 template <int NRT, int NTT, bool BUF, class Sink>
 __device__ __forceinline__ void block_partials(const float* __restrict__ x,
                                                const float* __restrict__ fn_w, int T, int n,
@@ -487,7 +471,7 @@ __device__ __forceinline__ void small_partials_groups(const float* __restrict__ 
 struct NoIssue {
   __device__ __forceinline__ void operator()() const {}
 };
-template <bool COHERENT = false, int BATCH = 8, class Issue = NoIssue>
+template <int BATCH = 8, class Issue = NoIssue>
 __device__ __forceinline__ void reduce_token_partials(const float* __restrict__ part, int G, int T,
                                                       int t, int RP, float* red256,
                                                       float* m_out, Issue issue = Issue()) {
@@ -504,7 +488,7 @@ __device__ __forceinline__ void reduce_token_partials(const float* __restrict__ 
 #pragma unroll
           for (int u = 0; u < BATCH; ++u) {
             const int g = g0 + u * Q;
-            v[u] = load_partial<COHERENT>(p + (size_t)(g < G ? g : q) * gstride);
+            v[u] = p[(size_t)(g < G ? g : q) * gstride];
           }
 #pragma unroll
           for (int u = 0; u < BATCH; ++u)
@@ -518,7 +502,7 @@ __device__ __forceinline__ void reduce_token_partials(const float* __restrict__ 
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
           const int g = q + u * Q;
-          v[u] = load_partial<COHERENT>(p + (size_t)(g < G ? g : q) * gstride);
+          v[u] = p[(size_t)(g < G ? g : q) * gstride];
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -532,7 +516,7 @@ __device__ __forceinline__ void reduce_token_partials(const float* __restrict__ 
 #pragma unroll
           for (int u = 0; u < BATCH; ++u) {
             const int g = g0 + u * Q;
-            v[u] = load_partial<COHERENT>(p + (size_t)(g < G ? g : q) * gstride);
+            v[u] = p[(size_t)(g < G ? g : q) * gstride];
           }
 #pragma unroll
           for (int u = 0; u < BATCH; ++u)

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(256) void head_finish_kernel(
       if (c < S) xq[c] = xt[(size_t)c * HQ + qa];
   }
 
-  reduce_token_partials<false, 16>(part, G, T, t, RP, red, m_raw);  // ends with a barrier
+  reduce_token_partials<16>(part, G, T, t, RP, red, m_raw);  // ends with a barrier
 
   float pc[8];
 #pragma unroll
