@@ -72,9 +72,10 @@ static hipError_t launch_partials_t(const float* x, const float* fn_w, int T, in
 }
 
 // Vector-ALU partials (S <= 4), every token's sums in the same order whatever
-// the group size, so a token's result does not depend on the batch it is in.  Grid: (G K-ranges, Y); block (g, y) takes the groups of
-// kSmallGroup tokens y, y + Y, ..., with the weight quads of its K-range held
-// in registers and the next group's x requested while the current one is
+// the group size, so a token's result does not depend on the batch it is in.
+// Grid: (G K-ranges, Y); block (g, y) takes the groups of kSmallGroup tokens
+// (one token at T = 1) y, y + Y, ..., with the weight quads of its K-range
+// held in registers and the next group's x requested while the current one is
 // reduced.  QL = column quads per lane (a K-range of at most 128*QL floats).
 constexpr int kSmallGroup = 4;
 constexpr int kSmallBlocks = 2048;  // target grid size at large T
